@@ -1,0 +1,187 @@
+/*
+ * rswa.h -- C ABI of the R-SWA (Reference Sliding Window Attention) library
+ * for AMD MI355X (gfx950).
+ *
+ * The method [page "开源5天Star破万之后：百度Unlimited-OCR的爆火路径复盘",
+ * www.gtnt.cn/news/146005, section 2.1 "环形滑窗注意力"]: the prefill tokens of
+ * a request (a document's image tokens plus its prompt) keep complete
+ * attention and are never evicted; decode keys/values are appended until the
+ * cache holds prefill_len + W entries; from then on each new token overwrites
+ * in place the ring slot prefill_len + ring_pos, ring_pos advancing by one
+ * modulo W, and attention runs over the whole cache, whose size therefore
+ * stays prefill_len + W however long the output grows.
+ *
+ * Positional encoding is not given on the pages.  This library rotates keys
+ * and queries with rotate-half RoPE (frequencies base^(-2i/D)) at the token's
+ * absolute position -- prefill token j at j, decode step s at
+ * prefill_len + s -- and stores keys already rotated.  ring_pos starts at 0
+ * on the first decode step, and the current token's key/value is written
+ * before its attention, so the ring window includes the current token.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All device pointers are HIP device memory owned by the caller.  The
+ *   library never allocates or frees device memory.  It allocates only the
+ *   host-side handle and a small pinned host staging area, both released by
+ *   rswa_cache_destroy.
+ * - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *   enqueued asynchronously on it; only rswa_cache_init and rswa_get_state
+ *   block.  Use one stream per handle.
+ * - Element type of every tensor is the config's dtype (bf16 or fp32).
+ * - Layouts (row-major, last index fastest):
+ *     pools         [num_layers][num_slots][num_heads][head_dim]
+ *     prefill q/k/v/out  [sum of prefill_len][num_heads][head_dim], packed
+ *                   in the order of req_ids
+ *     decode q/k/v/out   [n][num_heads][head_dim] in rswa_set_batch order
+ *   q and k are passed unrotated; the library applies RoPE.
+ * - Logical slot i (0 <= i < prefill_len + W) of a request lives at pool
+ *   row slot_base + i, or at pool row slot_table[slot_base + i] when the
+ *   config has a slot table (page-size-1 layout).
+ * - Every entry point validates on the host before launching anything.  A
+ *   call that returns an error launched nothing and changed no state;
+ *   rswa_last_error gives the reason.  No C++ exception crosses the ABI.
+ * - A handle is not thread-safe.
+ */
+#ifndef RSWA_H
+#define RSWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RSWA_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  RSWA_OK = 0,
+  RSWA_E_ARG = -1,         /* bad argument or config value */
+  RSWA_E_UNSUPPORTED = -2, /* head_dim / dtype combination not built */
+  RSWA_E_POSITION = -3,    /* a position would reach max_positions */
+  RSWA_E_CAPACITY = -4,    /* pool, slot table, workspace or batch too small */
+  RSWA_E_STATE = -5,       /* call out of order (see each entry point) */
+  RSWA_E_HIP = -6          /* a HIP runtime call failed */
+};
+
+enum { RSWA_DTYPE_BF16 = 0, RSWA_DTYPE_F32 = 1 };
+
+typedef struct rswa_config {
+  int32_t num_layers;     /* >= 1 */
+  int32_t num_heads;      /* >= 1; key/value heads = query heads */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t window;         /* W >= 1: generated tokens kept in the ring */
+  int32_t max_positions;  /* positions 0 .. max_positions-1; 0 means 32768 */
+  int32_t max_requests;   /* request ids are 0 .. max_requests-1 */
+  int64_t num_slots;      /* pool rows per layer */
+  int32_t dtype;          /* RSWA_DTYPE_BF16 or RSWA_DTYPE_F32 */
+  int32_t max_splits;     /* split-KV partial slots in the workspace;
+                             0 means max(16384, 4 * max_requests) */
+  int64_t max_prefill_tokens; /* largest sum of prefill_len in one
+                                 rswa_prefill call; 0 means 262144 */
+  int32_t decode_split_tokens; /* keys per split-KV work item, a multiple
+                                  of 64; 0 means chosen per batch */
+  int32_t reserved0;
+  double rope_base;       /* > 0; 0 means 10000 */
+  double softmax_scale;   /* <= 0 means 1/sqrt(head_dim) */
+  const int32_t *slot_table; /* device int32[slot_table_len] of pool rows,
+                                or NULL for contiguous rows.  Read once at
+                                init (entries must lie in [0, num_slots))
+                                and then by kernels; must not change while
+                                the handle lives. */
+  int64_t slot_table_len;
+} rswa_config;
+
+typedef struct rswa_cache rswa_cache;
+
+/* ABI version of the loaded library (RSWA_ABI_VERSION). */
+int rswa_abi_version(void);
+
+/* Bytes of device workspace rswa_cache_init needs for cfg (0 if cfg is
+ * invalid; rswa_last_error(NULL) then says why).  The workspace holds the
+ * RoPE table (computed in fp64 on the host, stored fp32), per-request device
+ * state, batch tables and split-KV partials. */
+size_t rswa_workspace_bytes(const rswa_config *cfg);
+
+/* Create a handle over caller-owned pools and workspace (256-byte aligned).
+ * k_pool / v_pool: device [num_layers][num_slots][num_heads][head_dim].
+ * Blocks: uploads the RoPE table and validates the slot table.
+ * Pool contents are not touched.  On success *out receives the handle. */
+int rswa_cache_init(const rswa_config *cfg, void *k_pool, void *v_pool,
+                    void *workspace, size_t workspace_bytes, void *stream,
+                    rswa_cache **out);
+
+/* Release the handle (host memory only).  Waits for the handle's pending
+ * staging copies.  NULL is accepted. */
+int rswa_cache_destroy(rswa_cache *c);
+
+/* Prefill one layer for n requests [section 2.1: complete attention over the
+ * prefill, nothing evicted; section 三 of the same page: the eager path does
+ * this with a full-matrix softmax].
+ * req_ids, prefill_len, slot_base: host arrays of n entries.  Layer 0
+ * (re)registers each request: prefill_len P >= 0, slot_base, and zero
+ * generated tokens; layers 1 .. num_layers-1 must then follow in order with
+ * the same values.  Needs P + W rows from slot_base (pool or table), and
+ * P <= max_positions.
+ * Writes pool rows of logical slots 0 .. P-1 of `layer`: K = RoPE(k, j),
+ * V = v.  Writes out[j] = causal attention of RoPE(q_j, j) over keys 0..j
+ * (scale softmax_scale).  q, k, v, out: device, packed as above. */
+int rswa_prefill(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids,
+                 const int32_t *prefill_len, const int64_t *slot_base,
+                 const void *q, const void *k, const void *v, void *out,
+                 void *stream);
+
+/* Select the active decode batch (host array of n distinct ids, each
+ * prefilled in every layer).  Plans the split-KV work for it.  Must not be
+ * called in the middle of a step (after a ring write, before advance). */
+int rswa_set_batch(rswa_cache *c, int32_t n, const int32_t *req_ids, void *stream);
+
+/* Ring write for `layer` [section 2.1: in-place overwrite of the ring slot].
+ * For active request b with P prefill tokens and t generated tokens so far:
+ * slot = P + (t mod W), position = P + t; K[slot] = RoPE(k_new[b], P + t),
+ * V[slot] = v_new[b].  Fails with RSWA_E_POSITION if P + t >= max_positions
+ * for any active request.  Once per layer per step, before rswa_decode_step
+ * of that layer. */
+int rswa_ring_write(rswa_cache *c, int32_t layer, const void *k_new,
+                    const void *v_new, void *stream);
+
+/* Decode attention for `layer` [section 2.1: attention over the whole cache
+ * after the write].  For active request b: out[b] = softmax attention of
+ * RoPE(q[b], P + t) over logical slots 0 .. L-1 with L = P + min(t + 1, W):
+ * the whole prefill and the newest min(t + 1, W) generated tokens.  Split-KV:
+ * partial (max, sum, vector) per split in the workspace, then a combine.
+ * Needs this step's rswa_ring_write(layer) first. */
+int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out,
+                     void *stream);
+
+/* End the step: t += 1 for every active request.  Needs rswa_decode_step of
+ * every layer in this step. */
+int rswa_advance(rswa_cache *c, void *stream);
+
+/* Read the device-side state of n registered requests (host arrays of n).
+ * ring_pos = t mod W (slot offset the next step writes), cache_len =
+ * P + min(t, W) (valid entries now), next_pos = P + t.  Any output pointer
+ * may be NULL.  Synchronizes `stream`; fails with RSWA_E_STATE if the device
+ * copy of t differs from the host's. */
+int rswa_get_state(rswa_cache *c, int32_t n, const int32_t *req_ids,
+                   int32_t *ring_pos, int32_t *cache_len, int32_t *next_pos,
+                   void *stream);
+
+/* Split-KV split size (keys per work item) and the number of decode work
+ * items planned for the current batch; 0s before rswa_set_batch. */
+int rswa_decode_plan(const rswa_cache *c, int32_t *split_tokens, int32_t *num_splits);
+
+/* Static name of a status code. */
+const char *rswa_status_string(int status);
+
+/* Message of the last failed call on c, or of the last failed handle-less
+ * call (rswa_workspace_bytes, rswa_cache_init) when c is NULL.  Valid until
+ * the next call on the same handle. */
+const char *rswa_last_error(const rswa_cache *c);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSWA_H */

@@ -1,0 +1,331 @@
+// Host-side model of an R-SWA handle (see host_state.hpp).  No HIP here.
+#include "host_state.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <numeric>
+
+namespace rswa {
+
+namespace {
+
+int fail(std::string *err, int code, const std::string &msg) {
+  if (err) *err = msg;
+  return code;
+}
+
+std::string S(int64_t v) { return std::to_string(v); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int resolve_config(const rswa_config &in, Config *out, std::string *err) {
+  Config c;
+  c.num_layers = in.num_layers;
+  c.num_heads = in.num_heads;
+  c.head_dim = in.head_dim;
+  c.window = in.window;
+  c.max_positions = in.max_positions == 0 ? kDefaultMaxPositions : in.max_positions;
+  c.max_requests = in.max_requests;
+  c.num_slots = in.num_slots;
+  c.dtype = in.dtype;
+  c.max_splits = in.max_splits == 0 ? std::max(16384, 4 * std::max(in.max_requests, 0))
+                                    : in.max_splits;
+  c.max_prefill_tokens =
+      in.max_prefill_tokens == 0 ? kDefaultMaxPrefillTokens : in.max_prefill_tokens;
+  c.decode_split_tokens = in.decode_split_tokens;
+  c.rope_base = in.rope_base == 0 ? 10000.0 : in.rope_base;
+  c.softmax_scale = in.softmax_scale > 0 ? in.softmax_scale : 0.0;
+  c.has_table = in.slot_table != nullptr;
+  c.slot_table_len = in.slot_table_len;
+
+  if (c.num_layers < 1) return fail(err, RSWA_E_ARG, "num_layers must be >= 1");
+  if (c.num_heads < 1 || c.num_heads > 512) return fail(err, RSWA_E_ARG, "num_heads must be in [1, 512]");
+  if (c.head_dim != 64 && c.head_dim != 128)
+    return fail(err, RSWA_E_UNSUPPORTED, "head_dim must be 64 or 128, got " + S(c.head_dim));
+  if (c.dtype != RSWA_DTYPE_BF16 && c.dtype != RSWA_DTYPE_F32)
+    return fail(err, RSWA_E_UNSUPPORTED, "dtype must be RSWA_DTYPE_BF16 or RSWA_DTYPE_F32");
+  if (c.window < 1) return fail(err, RSWA_E_ARG, "window must be >= 1");
+  if (c.max_positions < 1 || c.max_positions > (1 << 22))
+    return fail(err, RSWA_E_ARG, "max_positions must be in [1, 4194304]");
+  if (c.window > c.max_positions) return fail(err, RSWA_E_ARG, "window exceeds max_positions");
+  if (c.max_requests < 1 || c.max_requests > (1 << 20))
+    return fail(err, RSWA_E_ARG, "max_requests must be in [1, 1048576]");
+  if (c.num_slots < 1 || c.num_slots > INT32_MAX)
+    return fail(err, RSWA_E_ARG, "num_slots must be in [1, 2^31-1]");
+  if (c.max_splits < c.max_requests || c.max_splits > (1 << 24))
+    return fail(err, RSWA_E_ARG, "max_splits must be in [max_requests, 2^24]");
+  if ((int64_t)c.max_splits * c.num_heads > (int64_t(1) << 28))
+    return fail(err, RSWA_E_ARG, "max_splits * num_heads must be <= 2^28");
+  if (c.max_prefill_tokens < 1 || c.max_prefill_tokens > (int64_t(1) << 31))
+    return fail(err, RSWA_E_ARG, "max_prefill_tokens must be in [1, 2^31]");
+  if (c.decode_split_tokens < 0 || c.decode_split_tokens % kSplitQuantum != 0)
+    return fail(err, RSWA_E_ARG, "decode_split_tokens must be a non-negative multiple of 64");
+  if (!(c.rope_base > 0) || !std::isfinite(c.rope_base))
+    return fail(err, RSWA_E_ARG, "rope_base must be positive");
+  if (!std::isfinite(in.softmax_scale)) return fail(err, RSWA_E_ARG, "softmax_scale must be finite");
+  if (c.softmax_scale == 0) c.softmax_scale = 1.0 / std::sqrt((double)c.head_dim);
+  if (c.has_table) {
+    if (c.slot_table_len < 1 || c.slot_table_len > INT32_MAX)
+      return fail(err, RSWA_E_ARG, "slot_table_len must be in [1, 2^31-1] with a slot table");
+  } else if (in.slot_table_len != 0) {
+    return fail(err, RSWA_E_ARG, "slot_table_len given without a slot table");
+  }
+  *out = c;
+  return RSWA_OK;
+}
+
+BatchBlob BatchBlob::make(int n, int k) {
+  BatchBlob b;
+  b.req = 0;
+  b.split_off = align_up(sizeof(int32_t) * n, 16);
+  b.split_map = b.split_off + align_up(sizeof(int32_t) * (n + 1), 16);
+  b.bytes = b.split_map + align_up(sizeof(int32_t) * 2 * (size_t)k, 16);
+  return b;
+}
+
+size_t BatchBlob::capacity(const Config &c) { return make(c.max_requests, c.max_splits).bytes; }
+
+PrefillBlob PrefillBlob::make(int n, int64_t t) {
+  PrefillBlob b;
+  b.req = 0;
+  b.plen = align_up(sizeof(int32_t) * n, 16);
+  b.cu = b.plen + align_up(sizeof(int32_t) * n, 16);
+  b.base = b.cu + align_up(sizeof(int64_t) * (n + 1), 16);
+  b.tiles = b.base + align_up(sizeof(int64_t) * n, 16);
+  b.bytes = b.tiles + align_up(sizeof(int32_t) * 2 * (size_t)t, 16);
+  return b;
+}
+
+size_t PrefillBlob::capacity(const Config &c) {
+  return make(c.max_requests, c.max_prefill_tiles()).bytes;
+}
+
+Layout make_layout(const Config &c) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.rope = take(sizeof(float) * 2 * (size_t)c.max_positions * (c.head_dim / 2));
+  L.req_p = take(sizeof(int32_t) * c.max_requests);
+  L.req_t = take(sizeof(int32_t) * c.max_requests);
+  L.req_base = take(sizeof(int64_t) * c.max_requests);
+  L.batch_bytes = BatchBlob::capacity(c);
+  L.batch = take(L.batch_bytes);
+  L.part_o = take(sizeof(float) * (size_t)c.max_splits * c.num_heads * c.head_dim);
+  L.part_ml = take(sizeof(float) * 2 * (size_t)c.max_splits * c.num_heads);
+  L.prefill_bytes = PrefillBlob::capacity(c);
+  L.prefill = take(L.prefill_bytes);
+  L.total = off;
+  return L;
+}
+
+HostState::HostState(const Config &c)
+    : cfg_(c),
+      req_(c.max_requests),
+      in_batch_(c.max_requests, 0),
+      written_(c.num_layers, 0),
+      decoded_(c.num_layers, 0) {}
+
+bool HostState::step_open() const {
+  for (int l = 0; l < cfg_.num_layers; ++l)
+    if (written_[l] || decoded_[l]) return true;
+  return false;
+}
+
+int HostState::check_prefill(int32_t layer, int32_t n, const int32_t *ids, const int32_t *plen,
+                             const int64_t *base, std::string *err) const {
+  if (layer < 0 || layer >= cfg_.num_layers)
+    return fail(err, RSWA_E_ARG, "layer " + S(layer) + " out of range");
+  if (n < 0 || n > cfg_.max_requests) return fail(err, RSWA_E_ARG, "n out of range");
+  if (n > 0 && (!ids || !plen || !base)) return fail(err, RSWA_E_ARG, "null host array");
+  std::vector<uint8_t> seen(cfg_.max_requests, 0);
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    int32_t id = ids[i];
+    if (id < 0 || id >= cfg_.max_requests)
+      return fail(err, RSWA_E_ARG, "request id " + S(id) + " out of range");
+    if (seen[id]) return fail(err, RSWA_E_ARG, "request id " + S(id) + " repeated");
+    seen[id] = 1;
+    if (plen[i] < 0) return fail(err, RSWA_E_ARG, "negative prefill_len");
+    if (plen[i] > cfg_.max_positions)
+      return fail(err, RSWA_E_POSITION, "prefill_len " + S(plen[i]) + " exceeds max_positions");
+    if (base[i] < 0) return fail(err, RSWA_E_ARG, "negative slot_base");
+    if (base[i] + plen[i] + cfg_.window > cfg_.row_capacity())
+      return fail(err, RSWA_E_CAPACITY, "request " + S(id) + " needs rows up to " +
+                                            S(base[i] + plen[i] + cfg_.window) + " but the " +
+                                            (cfg_.has_table ? "slot table" : "pool") + " has " +
+                                            S(cfg_.row_capacity()));
+    total += plen[i];
+    if (in_batch_[id])
+      return fail(err, RSWA_E_STATE, "request " + S(id) + " is in the active decode batch");
+    const RequestState &r = req_[id];
+    if (layer > 0) {
+      if (r.plen < 0) return fail(err, RSWA_E_STATE, "request " + S(id) + " not registered at layer 0");
+      if (r.plen != plen[i] || r.base != base[i])
+        return fail(err, RSWA_E_STATE, "request " + S(id) + " prefill_len/slot_base differ from layer 0");
+      if (r.layers != layer)
+        return fail(err, RSWA_E_STATE, "request " + S(id) + " prefilled through layer " +
+                                           S(r.layers - 1) + "; layers must go in order");
+    }
+  }
+  if (total > cfg_.max_prefill_tokens)
+    return fail(err, RSWA_E_CAPACITY, "prefill tokens " + S(total) + " exceed max_prefill_tokens");
+  return RSWA_OK;
+}
+
+void HostState::commit_prefill(int32_t layer, int32_t n, const int32_t *ids, const int32_t *plen,
+                               const int64_t *base) {
+  for (int i = 0; i < n; ++i) {
+    RequestState &r = req_[ids[i]];
+    if (layer == 0) {
+      r.plen = plen[i];
+      r.base = base[i];
+      r.t = 0;
+      r.layers = 1;
+    } else {
+      r.layers = layer + 1;
+    }
+  }
+}
+
+PrefillPlan HostState::plan_prefill(int32_t n, const int32_t *plen, int32_t tile) const {
+  PrefillPlan p;
+  p.tile = tile;
+  p.cu.assign(n + 1, 0);
+  for (int b = 0; b < n; ++b) {
+    p.cu[b + 1] = p.cu[b] + plen[b];
+    p.max_len = std::max(p.max_len, plen[b]);
+  }
+  p.total_tokens = p.cu[n];
+  struct Item { int32_t b, qt; };
+  std::vector<Item> items;
+  for (int b = 0; b < n; ++b)
+    for (int32_t qt = 0; qt < ceil_div(plen[b], tile); ++qt) items.push_back({b, qt});
+  // Longest rows first: a causal query tile qt covers (qt + 1) * tile keys.
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item &a, const Item &b) { return a.qt > b.qt; });
+  p.tiles.reserve(items.size() * 2);
+  for (const Item &it : items) {
+    p.tiles.push_back(it.b);
+    p.tiles.push_back(it.qt);
+  }
+  return p;
+}
+
+int HostState::check_set_batch(int32_t n, const int32_t *ids, std::string *err) const {
+  if (step_open())
+    return fail(err, RSWA_E_STATE, "rswa_set_batch inside a step (after a ring write, before advance)");
+  if (n < 0 || n > cfg_.max_requests) return fail(err, RSWA_E_ARG, "n out of range");
+  if (n > 0 && !ids) return fail(err, RSWA_E_ARG, "null req_ids");
+  std::vector<uint8_t> seen(cfg_.max_requests, 0);
+  for (int i = 0; i < n; ++i) {
+    int32_t id = ids[i];
+    if (id < 0 || id >= cfg_.max_requests)
+      return fail(err, RSWA_E_ARG, "request id " + S(id) + " out of range");
+    if (seen[id]) return fail(err, RSWA_E_ARG, "request id " + S(id) + " repeated");
+    seen[id] = 1;
+    const RequestState &r = req_[id];
+    if (r.plen < 0 || r.layers != cfg_.num_layers)
+      return fail(err, RSWA_E_STATE, "request " + S(id) + " is not prefilled in every layer");
+  }
+  if (n > 0) {
+    DecodePlan p = plan_decode(n, ids);
+    if (p.num_splits() > cfg_.max_splits)
+      return fail(err, RSWA_E_CAPACITY, "batch needs " + S(p.num_splits()) +
+                                            " split work items; max_splits is " + S(cfg_.max_splits));
+  }
+  return RSWA_OK;
+}
+
+DecodePlan HostState::plan_decode(int32_t n, const int32_t *ids) const {
+  DecodePlan p;
+  // Longest cache a request reaches while decoding: prefill_len + W.
+  std::vector<int64_t> lmax(n);
+  int64_t sum = 0;
+  for (int b = 0; b < n; ++b) {
+    lmax[b] = (int64_t)req_[ids[b]].plen + cfg_.window;
+    sum += lmax[b];
+  }
+  int64_t s;
+  if (cfg_.decode_split_tokens > 0) {
+    s = cfg_.decode_split_tokens;
+  } else {
+    int64_t per_task = ceil_div(sum * cfg_.num_heads, kDefaultTargetTasks);
+    s = std::max<int64_t>(kSplitQuantum, ceil_div(per_task, kSplitQuantum) * kSplitQuantum);
+    auto count = [&](int64_t sz) {
+      int64_t k = 0;
+      for (int b = 0; b < n; ++b) k += ceil_div(lmax[b], sz);
+      return k;
+    };
+    while (count(s) > cfg_.max_splits) s += kSplitQuantum;
+  }
+  p.split_tokens = (int32_t)s;
+  p.split_off.assign(n + 1, 0);
+  for (int b = 0; b < n; ++b) {
+    int32_t k = (int32_t)ceil_div(lmax[b], s);
+    p.split_off[b + 1] = p.split_off[b] + k;
+    for (int32_t j = 0; j < k; ++j) {
+      p.split_map.push_back(b);
+      p.split_map.push_back(j);
+    }
+  }
+  return p;
+}
+
+void HostState::commit_set_batch(int32_t n, const int32_t *ids, DecodePlan plan) {
+  for (int32_t id : batch_) in_batch_[id] = 0;
+  batch_.assign(ids, ids + n);
+  for (int32_t id : batch_) in_batch_[id] = 1;
+  plan_ = std::move(plan);
+}
+
+int HostState::check_ring_write(int32_t layer, std::string *err) const {
+  if (layer < 0 || layer >= cfg_.num_layers)
+    return fail(err, RSWA_E_ARG, "layer " + S(layer) + " out of range");
+  if (batch_.empty()) return fail(err, RSWA_E_STATE, "no active batch (rswa_set_batch)");
+  if (written_[layer])
+    return fail(err, RSWA_E_STATE, "layer " + S(layer) + " already written in this step");
+  for (int32_t id : batch_) {
+    const RequestState &r = req_[id];
+    if ((int64_t)r.plen + r.t >= cfg_.max_positions)
+      return fail(err, RSWA_E_POSITION, "request " + S(id) + " reached position " +
+                                            S((int64_t)r.plen + r.t) + " = max_positions");
+  }
+  return RSWA_OK;
+}
+
+void HostState::commit_ring_write(int32_t layer) { written_[layer] = 1; }
+
+int HostState::check_decode(int32_t layer, std::string *err) const {
+  if (layer < 0 || layer >= cfg_.num_layers)
+    return fail(err, RSWA_E_ARG, "layer " + S(layer) + " out of range");
+  if (batch_.empty()) return fail(err, RSWA_E_STATE, "no active batch (rswa_set_batch)");
+  if (!written_[layer])
+    return fail(err, RSWA_E_STATE, "layer " + S(layer) + ": rswa_ring_write must come first");
+  if (decoded_[layer])
+    return fail(err, RSWA_E_STATE, "layer " + S(layer) + " already decoded in this step");
+  return RSWA_OK;
+}
+
+void HostState::commit_decode(int32_t layer) { decoded_[layer] = 1; }
+
+int HostState::check_advance(std::string *err) const {
+  if (batch_.empty()) return fail(err, RSWA_E_STATE, "no active batch (rswa_set_batch)");
+  for (int l = 0; l < cfg_.num_layers; ++l)
+    if (!decoded_[l])
+      return fail(err, RSWA_E_STATE, "layer " + S(l) + " not decoded in this step");
+  return RSWA_OK;
+}
+
+void HostState::commit_advance() {
+  for (int32_t id : batch_) req_[id].t += 1;
+  std::fill(written_.begin(), written_.end(), 0);
+  std::fill(decoded_.begin(), decoded_.end(), 0);
+}
+
+}  // namespace rswa

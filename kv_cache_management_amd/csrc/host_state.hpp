@@ -1,0 +1,155 @@
+// Host-side model of an R-SWA cache handle: config validation, workspace
+// layout, the per-request ring state mirror, the call-order state machine and
+// the split-KV / prefill work planning.  Pure C++17, no HIP: the same code is
+// linked into the HIP library and into a CPU-only test program.
+//
+// Ring state follows page "开源5天Star破万之后：百度Unlimited-OCR的爆火路径复盘"
+// (www.gtnt.cn/news/146005), section 2.1: a request holds its prefill_len
+// prefill rows plus a W-row ring written at prefill_len + ring_pos, so its
+// cache never exceeds prefill_len + W rows.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "rswa.h"
+
+namespace rswa {
+
+constexpr int kAlign = 256;
+constexpr int kSplitQuantum = 64;      // split sizes are multiples of this
+constexpr int kDefaultTargetTasks = 4096;
+constexpr int kDefaultMaxPositions = 32768;
+constexpr int64_t kDefaultMaxPrefillTokens = 262144;
+constexpr int kPrefillTileMin = 64;    // smallest prefill query tile of any kernel
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Config with defaults resolved.
+struct Config {
+  int32_t num_layers = 0, num_heads = 0, head_dim = 0, window = 0;
+  int32_t max_positions = 0, max_requests = 0, dtype = 0, max_splits = 0;
+  int32_t decode_split_tokens = 0;
+  int64_t num_slots = 0, max_prefill_tokens = 0, slot_table_len = 0;
+  double rope_base = 0, softmax_scale = 0;
+  bool has_table = false;
+  int elem_bytes() const { return dtype == RSWA_DTYPE_BF16 ? 2 : 4; }
+  int64_t row_capacity() const { return has_table ? slot_table_len : num_slots; }
+  int64_t max_prefill_tiles() const {
+    return max_prefill_tokens / kPrefillTileMin + max_requests;
+  }
+};
+
+// Byte offsets of each workspace region (all 256-byte aligned).
+struct Layout {
+  size_t rope = 0;        // float2 [max_positions][head_dim/2] (cos, sin)
+  size_t req_p = 0;       // int32 [max_requests]  prefill_len
+  size_t req_t = 0;       // int32 [max_requests]  generated tokens
+  size_t req_base = 0;    // int64 [max_requests]  slot_base
+  size_t batch = 0;       // batch blob (see BatchBlob)
+  size_t batch_bytes = 0;
+  size_t part_o = 0;      // float [max_splits][num_heads][head_dim]
+  size_t part_ml = 0;     // float2 [max_splits][num_heads]  (max, sum)
+  size_t prefill = 0;     // prefill blob (see PrefillBlob)
+  size_t prefill_bytes = 0;
+  size_t total = 0;
+};
+
+// Validates cfg and resolves defaults.  Returns RSWA_OK or an error code
+// with a message in *err.
+int resolve_config(const rswa_config &in, Config *out, std::string *err);
+Layout make_layout(const Config &c);
+
+// Offsets inside a packed blob uploaded in one copy.
+struct BatchBlob {   // for n active requests and k split work items
+  size_t req = 0;        // int32 [n]      request id of batch entry b
+  size_t split_off = 0;  // int32 [n + 1]  first split of batch entry b
+  size_t split_map = 0;  // int32 [2k]     (b, split index within b)
+  size_t bytes = 0;
+  static BatchBlob make(int n, int k);
+  static size_t capacity(const Config &c);
+};
+
+struct PrefillBlob {  // for n requests and t query tiles
+  size_t req = 0;        // int32 [n]
+  size_t plen = 0;       // int32 [n]
+  size_t cu = 0;         // int64 [n + 1]  packed token offset of request b
+  size_t base = 0;       // int64 [n]
+  size_t tiles = 0;      // int32 [2t]     (b, query tile index)
+  size_t bytes = 0;
+  static PrefillBlob make(int n, int64_t t);
+  static size_t capacity(const Config &c);
+};
+
+struct RequestState {
+  int32_t plen = -1;     // -1: never registered
+  int64_t base = 0;
+  int32_t t = 0;         // generated tokens already cached
+  int32_t layers = 0;    // layers prefilled (in order)
+};
+
+struct DecodePlan {
+  int32_t split_tokens = 0;
+  std::vector<int32_t> split_off;  // n + 1
+  std::vector<int32_t> split_map;  // 2 * num_splits
+  int32_t num_splits() const { return (int32_t)split_map.size() / 2; }
+};
+
+struct PrefillPlan {
+  int32_t tile = 0;
+  int64_t total_tokens = 0;
+  int32_t max_len = 0;
+  std::vector<int64_t> cu;         // n + 1
+  std::vector<int32_t> tiles;      // 2 * num_tiles, longest rows first
+  int64_t num_tiles() const { return (int64_t)tiles.size() / 2; }
+};
+
+// Call-order and ring bookkeeping of one handle.  Every check_* leaves the
+// state untouched; the matching commit_* applies a checked call.
+class HostState {
+ public:
+  explicit HostState(const Config &c);
+  const Config &config() const { return cfg_; }
+
+  int check_prefill(int32_t layer, int32_t n, const int32_t *ids, const int32_t *plen,
+                    const int64_t *base, std::string *err) const;
+  void commit_prefill(int32_t layer, int32_t n, const int32_t *ids, const int32_t *plen,
+                      const int64_t *base);
+  // Plans the packed offsets and the query tiles (of `tile` rows) of a
+  // checked prefill call.
+  PrefillPlan plan_prefill(int32_t n, const int32_t *plen, int32_t tile) const;
+
+  int check_set_batch(int32_t n, const int32_t *ids, std::string *err) const;
+  DecodePlan plan_decode(int32_t n, const int32_t *ids) const;
+  void commit_set_batch(int32_t n, const int32_t *ids, DecodePlan plan);
+
+  int check_ring_write(int32_t layer, std::string *err) const;
+  void commit_ring_write(int32_t layer);
+  int check_decode(int32_t layer, std::string *err) const;
+  void commit_decode(int32_t layer);
+  int check_advance(std::string *err) const;
+  void commit_advance();
+
+  const RequestState &request(int32_t id) const { return req_[id]; }
+  const std::vector<int32_t> &batch() const { return batch_; }
+  const DecodePlan &plan() const { return plan_; }
+  bool step_open() const;
+
+  // Closed forms of the ring bookkeeping for a request with t generated
+  // tokens already cached.
+  static int32_t ring_pos(int32_t t, int32_t w) { return t % w; }
+  static int32_t cache_len(int32_t p, int32_t t, int32_t w) { return p + (t < w ? t : w); }
+  static int32_t next_pos(int32_t p, int32_t t) { return p + t; }
+
+ private:
+  Config cfg_;
+  std::vector<RequestState> req_;
+  std::vector<uint8_t> in_batch_;
+  std::vector<int32_t> batch_;
+  DecodePlan plan_;
+  std::vector<uint8_t> written_, decoded_;
+};
+
+}  // namespace rswa

@@ -1,0 +1,86 @@
+// Launch interface between the C-ABI host layer and the gfx950 kernels.
+// Each launch_* enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace rswa {
+
+// Where a request's logical slot i lives: pool row table[base + i] when
+// table != nullptr, else row base + i.  Row r of layer l starts at element
+// l * layer_stride + r * heads * head_dim.
+struct PoolArgs {
+  void *k;
+  void *v;
+  int64_t layer_stride;   // elements per layer: num_slots * heads * head_dim
+  const int32_t *table;   // nullable
+};
+
+struct StateArgs {
+  int32_t *plen;          // [max_requests]
+  int32_t *t;             // [max_requests]
+  int64_t *base;          // [max_requests]
+};
+
+struct RingWriteArgs {
+  PoolArgs pool;
+  StateArgs st;
+  const int32_t *batch_req;   // [n]
+  const void *k_new;          // [n][H][D]
+  const void *v_new;
+  const float2 *rope;         // [max_positions][D/2]
+  int32_t n, heads, window, layer;
+};
+
+struct AdvanceArgs {
+  StateArgs st;
+  const int32_t *batch_req;
+  int32_t n;
+};
+
+struct DecodeArgs {
+  PoolArgs pool;
+  StateArgs st;
+  const int32_t *batch_req;   // [n]
+  const int32_t *split_map;   // [2 * num_splits] (batch entry, split index)
+  const int32_t *split_off;   // [n + 1]
+  const void *q;              // [n][H][D]
+  void *out;                  // [n][H][D]
+  float *part_o;              // [num_splits][H][D]
+  float2 *part_ml;            // [num_splits][H]  (running max in log2 units, sum)
+  const float2 *rope;
+  float qscale;               // softmax_scale * log2(e)
+  int32_t n, heads, window, layer, num_splits, split_tokens;
+};
+
+struct PrefillArgs {
+  PoolArgs pool;
+  StateArgs st;
+  const int32_t *req;         // [n]
+  const int32_t *plen;        // [n]
+  const int64_t *cu;          // [n + 1] packed token offsets
+  const int64_t *base;        // [n]
+  const int32_t *tiles;       // [2 * num_tiles] (batch entry, query tile)
+  const void *q;              // [total][H][D]
+  const void *k;
+  const void *v;
+  void *out;
+  const float2 *rope;
+  float qscale;
+  int32_t n, heads, layer, num_tiles, tile;
+  int64_t total_tokens;
+};
+
+// dtype: RSWA_DTYPE_BF16 or RSWA_DTYPE_F32; head_dim 64 or 128.
+hipError_t launch_ring_write(const RingWriteArgs &a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_advance(const AdvanceArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
+// Query-tile height the prefill attention kernel for (dtype, head_dim) uses.
+int prefill_tile_rows(int dtype, int head_dim);
+hipError_t launch_prefill_attention(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
+
+}  // namespace rswa

@@ -1,0 +1,443 @@
+// C ABI of the R-SWA library (declared in include/rswa.h): host validation
+// through HostState, workspace carving, uploads through a pinned staging
+// ring, and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "host_state.hpp"
+#include "kernels.hpp"
+#include "rswa.h"
+
+using rswa::Config;
+using rswa::HostState;
+using rswa::Layout;
+
+namespace {
+
+thread_local std::string g_last_error;
+constexpr int kStages = 4;
+
+int set_global_error(int code, const std::string &msg) {
+  g_last_error = msg;
+  return code;
+}
+
+}  // namespace
+
+struct rswa_cache {
+  Config cfg;
+  Layout lay;
+  HostState st;
+  void *k_pool = nullptr;
+  void *v_pool = nullptr;
+  char *ws = nullptr;
+  float qscale = 0.f;
+  std::string err;
+  char *staging[kStages] = {};
+  hipEvent_t staged[kStages] = {};
+  bool staged_live[kStages] = {};
+  int next_stage = 0;
+  size_t stage_bytes = 0;
+
+  explicit rswa_cache(const Config &c) : cfg(c), lay(rswa::make_layout(c)), st(c) {}
+
+  int fail(int code, const std::string &msg) {
+    err = msg;
+    return code;
+  }
+  int hip_fail(hipError_t e, const char *what) {
+    return fail(RSWA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  }
+
+  // Copy `bytes` of host data to device `dst` in stream order, through the
+  // next pinned staging slot (waiting only if that slot's previous copy is
+  // still pending).
+  hipError_t upload(void *dst, const void *src, size_t bytes, hipStream_t s) {
+    if (bytes == 0) return hipSuccess;
+    const int k = next_stage;
+    next_stage = (next_stage + 1) % kStages;
+    if (staged_live[k]) {
+      hipError_t e = hipEventSynchronize(staged[k]);
+      if (e != hipSuccess) return e;
+    }
+    std::memcpy(staging[k], src, bytes);
+    hipError_t e = hipMemcpyAsync(dst, staging[k], bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(staged[k], s);
+    staged_live[k] = (e == hipSuccess);
+    return e;
+  }
+
+  rswa::PoolArgs pool() const {
+    return {k_pool, v_pool, cfg.num_slots * cfg.num_heads * cfg.head_dim, nullptr};
+  }
+  rswa::StateArgs state() const {
+    return {(int32_t *)(ws + lay.req_p), (int32_t *)(ws + lay.req_t), (int64_t *)(ws + lay.req_base)};
+  }
+  const float2 *rope() const { return (const float2 *)(ws + lay.rope); }
+
+  const int32_t *slot_table = nullptr;
+};
+
+namespace {
+
+template <typename F>
+int guarded(rswa_cache *c, F &&f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc &) {
+    return c ? c->fail(RSWA_E_CAPACITY, "host allocation failed")
+             : set_global_error(RSWA_E_CAPACITY, "host allocation failed");
+  } catch (...) {
+    return c ? c->fail(RSWA_E_ARG, "internal error") : set_global_error(RSWA_E_ARG, "internal error");
+  }
+}
+
+// Append `count` values of T at byte offset `off` of blob.
+template <typename T>
+void put(std::vector<char> &blob, size_t off, const T *src, size_t count) {
+  if (count) std::memcpy(blob.data() + off, src, sizeof(T) * count);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rswa_abi_version(void) { return RSWA_ABI_VERSION; }
+
+const char *rswa_status_string(int status) {
+  switch (status) {
+    case RSWA_OK: return "RSWA_OK";
+    case RSWA_E_ARG: return "RSWA_E_ARG";
+    case RSWA_E_UNSUPPORTED: return "RSWA_E_UNSUPPORTED";
+    case RSWA_E_POSITION: return "RSWA_E_POSITION";
+    case RSWA_E_CAPACITY: return "RSWA_E_CAPACITY";
+    case RSWA_E_STATE: return "RSWA_E_STATE";
+    case RSWA_E_HIP: return "RSWA_E_HIP";
+    default: return "RSWA_E_UNKNOWN";
+  }
+}
+
+const char *rswa_last_error(const rswa_cache *c) {
+  return c ? c->err.c_str() : g_last_error.c_str();
+}
+
+size_t rswa_workspace_bytes(const rswa_config *cfg) {
+  if (!cfg) {
+    set_global_error(RSWA_E_ARG, "null config");
+    return 0;
+  }
+  Config c;
+  std::string err;
+  if (rswa::resolve_config(*cfg, &c, &err) != RSWA_OK) {
+    set_global_error(RSWA_E_ARG, err);
+    return 0;
+  }
+  return rswa::make_layout(c).total;
+}
+
+int rswa_cache_init(const rswa_config *cfg, void *k_pool, void *v_pool, void *workspace,
+                    size_t workspace_bytes, void *stream, rswa_cache **out) {
+  return guarded(nullptr, [&]() -> int {
+    if (!out) return set_global_error(RSWA_E_ARG, "null output handle pointer");
+    *out = nullptr;
+    if (!cfg) return set_global_error(RSWA_E_ARG, "null config");
+    Config c;
+    std::string err;
+    int rc = rswa::resolve_config(*cfg, &c, &err);
+    if (rc != RSWA_OK) return set_global_error(rc, err);
+    if (!k_pool || !v_pool || !workspace) return set_global_error(RSWA_E_ARG, "null pool or workspace");
+    if (((uintptr_t)k_pool | (uintptr_t)v_pool) % 16)
+      return set_global_error(RSWA_E_ARG, "pools must be 16-byte aligned");
+    if ((uintptr_t)workspace % rswa::kAlign)
+      return set_global_error(RSWA_E_ARG, "workspace must be 256-byte aligned");
+    Layout lay = rswa::make_layout(c);
+    if (workspace_bytes < lay.total)
+      return set_global_error(RSWA_E_CAPACITY, "workspace has " + std::to_string(workspace_bytes) +
+                                                   " bytes, needs " + std::to_string(lay.total));
+    hipStream_t s = (hipStream_t)stream;
+
+    // Slot table: every entry must name a pool row.
+    if (c.has_table) {
+      std::vector<int32_t> tab(c.slot_table_len);
+      hipError_t e = hipStreamSynchronize(s);
+      if (e == hipSuccess)
+        e = hipMemcpy(tab.data(), cfg->slot_table, sizeof(int32_t) * tab.size(), hipMemcpyDeviceToHost);
+      if (e != hipSuccess)
+        return set_global_error(RSWA_E_HIP, std::string("reading slot table: ") + hipGetErrorString(e));
+      for (size_t i = 0; i < tab.size(); ++i)
+        if (tab[i] < 0 || tab[i] >= c.num_slots)
+          return set_global_error(RSWA_E_ARG, "slot_table[" + std::to_string(i) + "] = " +
+                                                  std::to_string(tab[i]) + " is not a pool row");
+    }
+
+    // RoPE table, computed in fp64 and stored fp32: angle p * base^(-2i/D).
+    const int half = c.head_dim / 2;
+    std::vector<float> rope((size_t)c.max_positions * half * 2);
+    std::vector<double> freq(half);
+    for (int i = 0; i < half; ++i) freq[i] = std::pow(c.rope_base, -2.0 * i / c.head_dim);
+    for (int64_t p = 0; p < c.max_positions; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)p * freq[i];
+        rope[(p * half + i) * 2] = (float)std::cos(ang);
+        rope[(p * half + i) * 2 + 1] = (float)std::sin(ang);
+      }
+
+    rswa_cache *h = new rswa_cache(c);
+    h->k_pool = k_pool;
+    h->v_pool = v_pool;
+    h->ws = (char *)workspace;
+    h->slot_table = cfg->slot_table;
+    h->qscale = (float)(c.softmax_scale * 1.4426950408889634);  // scale * log2(e)
+    h->stage_bytes = std::max(rswa::BatchBlob::capacity(c), rswa::PrefillBlob::capacity(c));
+    auto cleanup = [&](hipError_t e, const char *what) {
+      std::string msg = std::string(what) + ": " + hipGetErrorString(e);
+      rswa_cache_destroy(h);
+      return set_global_error(RSWA_E_HIP, msg);
+    };
+    for (int k = 0; k < kStages; ++k) {
+      hipError_t e = hipHostMalloc((void **)&h->staging[k], h->stage_bytes, hipHostMallocDefault);
+      if (e != hipSuccess) return cleanup(e, "hipHostMalloc");
+      e = hipEventCreateWithFlags(&h->staged[k], hipEventDisableTiming);
+      if (e != hipSuccess) return cleanup(e, "hipEventCreate");
+    }
+    hipError_t e = hipMemcpyAsync(h->ws + lay.rope, rope.data(), sizeof(float) * rope.size(),
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.req_p, 0xff, sizeof(int32_t) * c.max_requests, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.req_t, 0, sizeof(int32_t) * c.max_requests, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.req_base, 0, sizeof(int64_t) * c.max_requests, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return cleanup(e, "uploading the RoPE table");
+    *out = h;
+    return RSWA_OK;
+  });
+}
+
+int rswa_cache_destroy(rswa_cache *c) {
+  if (!c) return RSWA_OK;
+  for (int k = 0; k < kStages; ++k) {
+    if (c->staged[k]) {
+      if (c->staged_live[k]) (void)hipEventSynchronize(c->staged[k]);
+      (void)hipEventDestroy(c->staged[k]);
+    }
+    if (c->staging[k]) (void)hipHostFree(c->staging[k]);
+  }
+  delete c;
+  return RSWA_OK;
+}
+
+int rswa_prefill(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids,
+                 const int32_t *prefill_len, const int64_t *slot_base, const void *q, const void *k,
+                 const void *v, void *out, void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    std::string err;
+    int rc = c->st.check_prefill(layer, n, req_ids, prefill_len, slot_base, &err);
+    if (rc != RSWA_OK) return c->fail(rc, err);
+    const Config &cf = c->cfg;
+    const int tile = rswa::prefill_tile_rows(cf.dtype, cf.head_dim);
+    rswa::PrefillPlan plan = c->st.plan_prefill(n, prefill_len, tile);
+    if (plan.total_tokens > 0 && (!q || !k || !v || !out))
+      return c->fail(RSWA_E_ARG, "null q/k/v/out with prefill tokens");
+    if (plan.num_tiles() > cf.max_prefill_tiles())
+      return c->fail(RSWA_E_CAPACITY, "too many prefill tiles");
+    hipStream_t s = (hipStream_t)stream;
+
+    rswa::PrefillBlob pb = rswa::PrefillBlob::make(n, plan.num_tiles());
+    std::vector<char> blob(pb.bytes, 0);
+    put(blob, pb.req, req_ids, n);
+    put(blob, pb.plen, prefill_len, n);
+    put(blob, pb.cu, plan.cu.data(), n + 1);
+    put(blob, pb.base, slot_base, n);
+    put(blob, pb.tiles, plan.tiles.data(), plan.tiles.size());
+    char *dev = c->ws + c->lay.prefill;
+    hipError_t e = c->upload(dev, blob.data(), pb.bytes, s);
+    if (e != hipSuccess) return c->hip_fail(e, "prefill metadata upload");
+
+    rswa::PrefillArgs a{};
+    a.pool = c->pool();
+    a.pool.table = c->slot_table;
+    a.st = c->state();
+    a.req = (const int32_t *)(dev + pb.req);
+    a.plen = (const int32_t *)(dev + pb.plen);
+    a.cu = (const int64_t *)(dev + pb.cu);
+    a.base = (const int64_t *)(dev + pb.base);
+    a.tiles = (const int32_t *)(dev + pb.tiles);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.rope = c->rope();
+    a.qscale = c->qscale;
+    a.n = n;
+    a.heads = cf.num_heads;
+    a.layer = layer;
+    a.num_tiles = (int32_t)plan.num_tiles();
+    a.tile = tile;
+    a.total_tokens = plan.total_tokens;
+    if (layer == 0) {
+      e = rswa::launch_prefill_register(a, s);
+      if (e != hipSuccess) return c->hip_fail(e, "prefill register launch");
+    }
+    e = rswa::launch_prefill_cache_write(a, cf.dtype, cf.head_dim, s);
+    if (e != hipSuccess) return c->hip_fail(e, "prefill cache write launch");
+    e = rswa::launch_prefill_attention(a, cf.dtype, cf.head_dim, s);
+    if (e != hipSuccess) return c->hip_fail(e, "prefill attention launch");
+    c->st.commit_prefill(layer, n, req_ids, prefill_len, slot_base);
+    return RSWA_OK;
+  });
+}
+
+int rswa_set_batch(rswa_cache *c, int32_t n, const int32_t *req_ids, void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    std::string err;
+    int rc = c->st.check_set_batch(n, req_ids, &err);
+    if (rc != RSWA_OK) return c->fail(rc, err);
+    rswa::DecodePlan plan;
+    if (n > 0) {
+      plan = c->st.plan_decode(n, req_ids);
+      rswa::BatchBlob bb = rswa::BatchBlob::make(n, plan.num_splits());
+      std::vector<char> blob(bb.bytes, 0);
+      put(blob, bb.req, req_ids, n);
+      put(blob, bb.split_off, plan.split_off.data(), n + 1);
+      put(blob, bb.split_map, plan.split_map.data(), plan.split_map.size());
+      hipError_t e = c->upload(c->ws + c->lay.batch, blob.data(), bb.bytes, (hipStream_t)stream);
+      if (e != hipSuccess) return c->hip_fail(e, "batch upload");
+    }
+    c->st.commit_set_batch(n, req_ids, std::move(plan));
+    return RSWA_OK;
+  });
+}
+
+int rswa_ring_write(rswa_cache *c, int32_t layer, const void *k_new, const void *v_new,
+                    void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    std::string err;
+    int rc = c->st.check_ring_write(layer, &err);
+    if (rc != RSWA_OK) return c->fail(rc, err);
+    if (!k_new || !v_new) return c->fail(RSWA_E_ARG, "null k_new / v_new");
+    rswa::BatchBlob bb = rswa::BatchBlob::make((int)c->st.batch().size(), c->st.plan().num_splits());
+    rswa::RingWriteArgs a{};
+    a.pool = c->pool();
+    a.pool.table = c->slot_table;
+    a.st = c->state();
+    a.batch_req = (const int32_t *)(c->ws + c->lay.batch + bb.req);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.rope = c->rope();
+    a.n = (int32_t)c->st.batch().size();
+    a.heads = c->cfg.num_heads;
+    a.window = c->cfg.window;
+    a.layer = layer;
+    hipError_t e = rswa::launch_ring_write(a, c->cfg.dtype, c->cfg.head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return c->hip_fail(e, "ring write launch");
+    c->st.commit_ring_write(layer);
+    return RSWA_OK;
+  });
+}
+
+int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out, void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    std::string err;
+    int rc = c->st.check_decode(layer, &err);
+    if (rc != RSWA_OK) return c->fail(rc, err);
+    if (!q || !out) return c->fail(RSWA_E_ARG, "null q / out");
+    const rswa::DecodePlan &plan = c->st.plan();
+    const int n = (int)c->st.batch().size();
+    rswa::BatchBlob bb = rswa::BatchBlob::make(n, plan.num_splits());
+    const char *dev = c->ws + c->lay.batch;
+    rswa::DecodeArgs a{};
+    a.pool = c->pool();
+    a.pool.table = c->slot_table;
+    a.st = c->state();
+    a.batch_req = (const int32_t *)(dev + bb.req);
+    a.split_map = (const int32_t *)(dev + bb.split_map);
+    a.split_off = (const int32_t *)(dev + bb.split_off);
+    a.q = q;
+    a.out = out;
+    a.part_o = (float *)(c->ws + c->lay.part_o);
+    a.part_ml = (float2 *)(c->ws + c->lay.part_ml);
+    a.rope = c->rope();
+    a.qscale = c->qscale;
+    a.n = n;
+    a.heads = c->cfg.num_heads;
+    a.window = c->cfg.window;
+    a.layer = layer;
+    a.num_splits = plan.num_splits();
+    a.split_tokens = plan.split_tokens;
+    hipError_t e = rswa::launch_decode(a, c->cfg.dtype, c->cfg.head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return c->hip_fail(e, "decode launch");
+    c->st.commit_decode(layer);
+    return RSWA_OK;
+  });
+}
+
+int rswa_advance(rswa_cache *c, void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    std::string err;
+    int rc = c->st.check_advance(&err);
+    if (rc != RSWA_OK) return c->fail(rc, err);
+    rswa::BatchBlob bb = rswa::BatchBlob::make((int)c->st.batch().size(), c->st.plan().num_splits());
+    rswa::AdvanceArgs a{};
+    a.st = c->state();
+    a.batch_req = (const int32_t *)(c->ws + c->lay.batch + bb.req);
+    a.n = (int32_t)c->st.batch().size();
+    hipError_t e = rswa::launch_advance(a, (hipStream_t)stream);
+    if (e != hipSuccess) return c->hip_fail(e, "advance launch");
+    c->st.commit_advance();
+    return RSWA_OK;
+  });
+}
+
+int rswa_get_state(rswa_cache *c, int32_t n, const int32_t *req_ids, int32_t *ring_pos,
+                   int32_t *cache_len, int32_t *next_pos, void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    const Config &cf = c->cfg;
+    if (n < 0 || (n > 0 && !req_ids)) return c->fail(RSWA_E_ARG, "bad n / req_ids");
+    for (int i = 0; i < n; ++i) {
+      if (req_ids[i] < 0 || req_ids[i] >= cf.max_requests)
+        return c->fail(RSWA_E_ARG, "request id out of range");
+      if (c->st.request(req_ids[i]).plen < 0)
+        return c->fail(RSWA_E_STATE, "request " + std::to_string(req_ids[i]) + " not registered");
+    }
+    std::vector<int32_t> dp(cf.max_requests), dt(cf.max_requests);
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess)
+      e = hipMemcpy(dp.data(), c->ws + c->lay.req_p, sizeof(int32_t) * dp.size(), hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+      e = hipMemcpy(dt.data(), c->ws + c->lay.req_t, sizeof(int32_t) * dt.size(), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return c->hip_fail(e, "reading device state");
+    for (int i = 0; i < n; ++i) {
+      const rswa::RequestState &r = c->st.request(req_ids[i]);
+      const int32_t p = dp[req_ids[i]], t = dt[req_ids[i]];
+      if (p != r.plen || t != r.t)
+        return c->fail(RSWA_E_STATE, "device state of request " + std::to_string(req_ids[i]) +
+                                         " (P=" + std::to_string(p) + ", t=" + std::to_string(t) +
+                                         ") differs from the host's (P=" + std::to_string(r.plen) +
+                                         ", t=" + std::to_string(r.t) + ")");
+      if (ring_pos) ring_pos[i] = HostState::ring_pos(t, cf.window);
+      if (cache_len) cache_len[i] = HostState::cache_len(p, t, cf.window);
+      if (next_pos) next_pos[i] = HostState::next_pos(p, t);
+    }
+    return RSWA_OK;
+  });
+}
+
+int rswa_decode_plan(const rswa_cache *c, int32_t *split_tokens, int32_t *num_splits) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  if (split_tokens) *split_tokens = c->st.plan().split_tokens;
+  if (num_splits) *num_splits = c->st.plan().num_splits();
+  return RSWA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,338 @@
+"""ctypes binding of librswa.so (the C ABI in include/rswa.h).
+
+The functions below carry the C names and only marshal arguments; every step
+of the hot path runs in the library's HIP kernels.  ``RSWACache`` is a small
+convenience wrapper that allocates the pools and workspace with torch and
+passes tensor pointers and torch's current HIP stream through.
+
+The library must already be built (``python -m kv_cache_management_amd.build``);
+loading fails loudly otherwise.  torch is imported first so that the process
+holds a single HIP runtime, shared by torch and the library.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librswa.so")
+
+RSWA_OK = 0
+RSWA_E_ARG = -1
+RSWA_E_UNSUPPORTED = -2
+RSWA_E_POSITION = -3
+RSWA_E_CAPACITY = -4
+RSWA_E_STATE = -5
+RSWA_E_HIP = -6
+RSWA_DTYPE_BF16 = 0
+RSWA_DTYPE_F32 = 1
+
+EXPORTED = (
+    "rswa_abi_version", "rswa_workspace_bytes", "rswa_cache_init", "rswa_cache_destroy",
+    "rswa_prefill", "rswa_set_batch", "rswa_ring_write", "rswa_decode_step",
+    "rswa_advance", "rswa_get_state", "rswa_decode_plan", "rswa_status_string",
+    "rswa_last_error",
+)
+
+
+class rswa_config(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("max_positions", ctypes.c_int32),
+        ("max_requests", ctypes.c_int32),
+        ("num_slots", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("max_prefill_tokens", ctypes.c_int64),
+        ("decode_split_tokens", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("softmax_scale", ctypes.c_double),
+        ("slot_table", ctypes.c_void_p),
+        ("slot_table_len", ctypes.c_int64),
+    ]
+
+
+class RSWAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def _single_hip_runtime():
+    """Paths of every libamdhip64 mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def load():
+    """Load librswa.so once (after torch) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- torch's HIP runtime first
+
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m kv_cache_management_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+    runtimes = _single_hip_runtime()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"more than one HIP runtime mapped: {sorted(runtimes)}")
+    P = ctypes.c_void_p
+    I32 = ctypes.c_int32
+    pI32 = ctypes.POINTER(ctypes.c_int32)
+    pI64 = ctypes.POINTER(ctypes.c_int64)
+    pcfg = ctypes.POINTER(rswa_config)
+    sig = {
+        "rswa_abi_version": (ctypes.c_int, []),
+        "rswa_workspace_bytes": (ctypes.c_size_t, [pcfg]),
+        "rswa_cache_init": (ctypes.c_int, [pcfg, P, P, P, ctypes.c_size_t, P, ctypes.POINTER(P)]),
+        "rswa_cache_destroy": (ctypes.c_int, [P]),
+        "rswa_prefill": (ctypes.c_int, [P, I32, I32, pI32, pI32, pI64, P, P, P, P, P]),
+        "rswa_set_batch": (ctypes.c_int, [P, I32, pI32, P]),
+        "rswa_ring_write": (ctypes.c_int, [P, I32, P, P, P]),
+        "rswa_decode_step": (ctypes.c_int, [P, I32, P, P, P]),
+        "rswa_advance": (ctypes.c_int, [P, P]),
+        "rswa_get_state": (ctypes.c_int, [P, I32, pI32, pI32, pI32, pI32, P]),
+        "rswa_decode_plan": (ctypes.c_int, [P, pI32, pI32]),
+        "rswa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "rswa_last_error": (ctypes.c_char_p, [P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_name(status: int) -> str:
+    return load().rswa_status_string(status).decode()
+
+
+def _i32(a) -> ctypes.Array:
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _i64(a):
+    a = np.ascontiguousarray(a, dtype=np.int64)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+# ---------------------------------------------------------------- C names
+
+def rswa_abi_version() -> int:
+    return load().rswa_abi_version()
+
+
+def rswa_workspace_bytes(cfg: rswa_config) -> int:
+    return load().rswa_workspace_bytes(ctypes.byref(cfg))
+
+
+def rswa_cache_init(cfg, k_pool: int, v_pool: int, workspace: int, workspace_bytes: int,
+                    stream: int):
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    st = load().rswa_cache_init(ctypes.byref(cfg), k_pool, v_pool, workspace, workspace_bytes,
+                                stream, ctypes.byref(h))
+    return st, h.value
+
+
+def rswa_cache_destroy(handle) -> int:
+    return load().rswa_cache_destroy(handle)
+
+
+def rswa_prefill(handle, layer: int, req_ids, prefill_len, slot_base, q: int, k: int, v: int,
+                 out: int, stream: int) -> int:
+    ids, pids = _i32(req_ids)
+    pl, ppl = _i32(prefill_len)
+    sb, psb = _i64(slot_base)
+    return load().rswa_prefill(handle, layer, len(ids), pids, ppl, psb, q, k, v, out, stream)
+
+
+def rswa_set_batch(handle, req_ids, stream: int) -> int:
+    ids, pids = _i32(req_ids)
+    return load().rswa_set_batch(handle, len(ids), pids, stream)
+
+
+def rswa_ring_write(handle, layer: int, k_new: int, v_new: int, stream: int) -> int:
+    return load().rswa_ring_write(handle, layer, k_new, v_new, stream)
+
+
+def rswa_decode_step(handle, layer: int, q: int, out: int, stream: int) -> int:
+    return load().rswa_decode_step(handle, layer, q, out, stream)
+
+
+def rswa_advance(handle, stream: int) -> int:
+    return load().rswa_advance(handle, stream)
+
+
+def rswa_get_state(handle, req_ids, stream: int):
+    """Returns (status, ring_pos, cache_len, next_pos) as int32 arrays."""
+    ids, pids = _i32(req_ids)
+    n = len(ids)
+    rp, prp = _i32(np.zeros(n))
+    cl, pcl = _i32(np.zeros(n))
+    npz, pnp = _i32(np.zeros(n))
+    st = load().rswa_get_state(handle, n, pids, prp, pcl, pnp, stream)
+    return st, rp, cl, npz
+
+
+def rswa_decode_plan(handle):
+    s = ctypes.c_int32()
+    k = ctypes.c_int32()
+    st = load().rswa_decode_plan(handle, ctypes.byref(s), ctypes.byref(k))
+    return st, s.value, k.value
+
+
+def rswa_status_string(status: int) -> str:
+    return status_name(status)
+
+
+def rswa_last_error(handle=None) -> str:
+    return load().rswa_last_error(handle).decode()
+
+
+# ------------------------------------------------------- torch convenience
+
+class RSWACache:
+    """Pools + workspace allocated with torch on the current device.
+
+    Pools: [num_layers][num_slots][heads][head_dim] of `dtype`; a slot table
+    (numpy int32) selects the page-size-1 layout.  Every method raises
+    RSWAError on a non-zero status.
+    """
+
+    def __init__(self, num_layers: int, num_heads: int, head_dim: int, window: int,
+                 max_requests: int, num_slots: int, dtype: str = "bf16",
+                 max_positions: int = 32768, rope_base: float = 10000.0,
+                 softmax_scale: float = 0.0, slot_table: Optional[np.ndarray] = None,
+                 max_prefill_tokens: int = 0, max_splits: int = 0,
+                 decode_split_tokens: int = 0, pool_fill: Optional[float] = None,
+                 device: str = "cuda"):
+        import torch
+
+        self.torch = torch
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.dtype = dtype
+        self.num_layers, self.heads, self.head_dim, self.window = num_layers, num_heads, head_dim, window
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        cfg = rswa_config()
+        cfg.num_layers = num_layers
+        cfg.num_heads = num_heads
+        cfg.head_dim = head_dim
+        cfg.window = window
+        cfg.max_positions = max_positions
+        cfg.max_requests = max_requests
+        cfg.num_slots = num_slots
+        cfg.dtype = RSWA_DTYPE_BF16 if dtype == "bf16" else RSWA_DTYPE_F32
+        cfg.max_splits = max_splits
+        cfg.max_prefill_tokens = max_prefill_tokens
+        cfg.decode_split_tokens = decode_split_tokens
+        cfg.rope_base = rope_base
+        cfg.softmax_scale = softmax_scale
+        shape = (num_layers, num_slots, num_heads, head_dim)
+        if pool_fill is None:
+            self.k_pool = torch.empty(shape, dtype=self.tdtype, device=self.device)
+            self.v_pool = torch.empty(shape, dtype=self.tdtype, device=self.device)
+        else:
+            self.k_pool = torch.full(shape, pool_fill, dtype=self.tdtype, device=self.device)
+            self.v_pool = torch.full(shape, pool_fill, dtype=self.tdtype, device=self.device)
+        if slot_table is not None:
+            self.slot_table = torch.from_numpy(np.ascontiguousarray(slot_table, np.int32)).to(self.device)
+            cfg.slot_table = self.slot_table.data_ptr()
+            cfg.slot_table_len = self.slot_table.numel()
+        else:
+            self.slot_table = None
+        self.cfg = cfg
+        nbytes = rswa_workspace_bytes(cfg)
+        if nbytes == 0:
+            raise RSWAError(RSWA_E_ARG, rswa_last_error(None))
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        ws = self.workspace.data_ptr()
+        ws_aligned = (ws + 255) // 256 * 256
+        st, h = rswa_cache_init(cfg, self.k_pool.data_ptr(), self.v_pool.data_ptr(), ws_aligned,
+                                nbytes, self.stream())
+        if st != RSWA_OK:
+            raise RSWAError(st, rswa_last_error(None))
+        self.handle = h
+
+    def stream(self) -> int:
+        return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    def _check(self, st: int):
+        if st != RSWA_OK:
+            raise RSWAError(st, rswa_last_error(self.handle))
+
+    def _ptr(self, t, shape):
+        if t.dtype != self.tdtype or not t.is_contiguous() or t.device != self.device:
+            raise ValueError("tensor must be contiguous, on the cache's device, of the cache's dtype")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"expected shape {tuple(shape)}, got {tuple(t.shape)}")
+        return t.data_ptr()
+
+    def prefill(self, layer: int, req_ids: Sequence[int], prefill_len: Sequence[int],
+                slot_base: Sequence[int], q, k, v, out):
+        total = int(np.sum(prefill_len)) if len(prefill_len) else 0
+        shp = (total, self.heads, self.head_dim)
+        self._check(rswa_prefill(self.handle, layer, req_ids, prefill_len, slot_base,
+                                 self._ptr(q, shp), self._ptr(k, shp), self._ptr(v, shp),
+                                 self._ptr(out, shp), self.stream()))
+
+    def set_batch(self, req_ids: Sequence[int]):
+        self._check(rswa_set_batch(self.handle, req_ids, self.stream()))
+        self.n = len(req_ids)
+
+    def ring_write(self, layer: int, k_new, v_new):
+        shp = (self.n, self.heads, self.head_dim)
+        self._check(rswa_ring_write(self.handle, layer, self._ptr(k_new, shp),
+                                    self._ptr(v_new, shp), self.stream()))
+
+    def decode_step(self, layer: int, q, out):
+        shp = (self.n, self.heads, self.head_dim)
+        self._check(rswa_decode_step(self.handle, layer, self._ptr(q, shp), self._ptr(out, shp),
+                                     self.stream()))
+
+    def advance(self):
+        self._check(rswa_advance(self.handle, self.stream()))
+
+    def get_state(self, req_ids: Sequence[int]):
+        st, rp, cl, npos = rswa_get_state(self.handle, req_ids, self.stream())
+        self._check(st)
+        return rp, cl, npos
+
+    def decode_plan(self):
+        st, s, k = rswa_decode_plan(self.handle)
+        self._check(st)
+        return s, k
+
+    def close(self):
+        if getattr(self, "handle", None):
+            rswa_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,263 @@
+// CPU test of the host-side R-SWA state machine and planners (no HIP).
+// Built with g++ and AddressSanitizer/UBSan by tests/test_host_state.py.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <deque>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "host_state.hpp"
+
+using namespace rswa;
+
+static int g_fail = 0;
+#define CHECK(cond)                                                     \
+  do {                                                                  \
+    if (!(cond)) {                                                      \
+      std::fprintf(stderr, "%s:%d CHECK failed: %s\n", __FILE__, __LINE__, #cond); \
+      ++g_fail;                                                         \
+    }                                                                   \
+  } while (0)
+
+static rswa_config base_cfg() {
+  rswa_config c{};
+  c.num_layers = 2;
+  c.num_heads = 10;
+  c.head_dim = 128;
+  c.window = 8;
+  c.max_positions = 1000;
+  c.max_requests = 4;
+  c.num_slots = 4000;
+  c.dtype = RSWA_DTYPE_BF16;
+  return c;
+}
+
+static Config resolved(const rswa_config &in) {
+  Config c;
+  std::string err;
+  int rc = resolve_config(in, &c, &err);
+  if (rc != RSWA_OK) std::fprintf(stderr, "resolve: %s\n", err.c_str());
+  CHECK(rc == RSWA_OK);
+  return c;
+}
+
+static void test_config() {
+  std::string err;
+  Config out;
+  auto bad = [&](auto mut, int code) {
+    rswa_config c = base_cfg();
+    mut(c);
+    int rc = resolve_config(c, &out, &err);
+    CHECK(rc == code);
+    CHECK(!err.empty());
+    err.clear();
+  };
+  bad([](rswa_config &c) { c.num_layers = 0; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.num_heads = 0; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.head_dim = 96; }, RSWA_E_UNSUPPORTED);
+  bad([](rswa_config &c) { c.dtype = 7; }, RSWA_E_UNSUPPORTED);
+  bad([](rswa_config &c) { c.window = 0; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.window = 2000; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.max_requests = 0; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.num_slots = 0; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.max_splits = 2; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.decode_split_tokens = 100; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.rope_base = -1; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.slot_table_len = 5; }, RSWA_E_ARG);
+  bad([](rswa_config &c) { c.slot_table = (const int32_t *)16; c.slot_table_len = 0; }, RSWA_E_ARG);
+  rswa_config c = base_cfg();
+  c.max_positions = 0;
+  c.rope_base = 0;
+  c.softmax_scale = 0;
+  Config r = resolved(c);
+  CHECK(r.max_positions == 32768);
+  CHECK(r.rope_base == 10000.0);
+  CHECK(r.softmax_scale > 0.0883 && r.softmax_scale < 0.0884);
+  CHECK(r.max_splits == 16384);
+}
+
+static void test_layout() {
+  Config c = resolved(base_cfg());
+  Layout L = make_layout(c);
+  struct R { size_t off, len; };
+  std::vector<R> rs = {
+      {L.rope, sizeof(float) * 2 * c.max_positions * (c.head_dim / 2)},
+      {L.req_p, 4u * c.max_requests},
+      {L.req_t, 4u * c.max_requests},
+      {L.req_base, 8u * c.max_requests},
+      {L.batch, L.batch_bytes},
+      {L.part_o, sizeof(float) * c.max_splits * c.num_heads * c.head_dim},
+      {L.part_ml, sizeof(float) * 2 * c.max_splits * c.num_heads},
+      {L.prefill, L.prefill_bytes}};
+  std::sort(rs.begin(), rs.end(), [](R a, R b) { return a.off < b.off; });
+  for (size_t i = 0; i < rs.size(); ++i) {
+    CHECK(rs[i].off % kAlign == 0);
+    CHECK(rs[i].off + rs[i].len <= (i + 1 < rs.size() ? rs[i + 1].off : L.total));
+  }
+  // blobs fit their regions at capacity
+  CHECK(BatchBlob::make(c.max_requests, c.max_splits).bytes <= L.batch_bytes);
+  CHECK(PrefillBlob::make(c.max_requests, c.max_prefill_tiles()).bytes <= L.prefill_bytes);
+}
+
+static void test_prefill_order_and_errors() {
+  Config c = resolved(base_cfg());
+  HostState st(c);
+  std::string err;
+  int32_t ids[2] = {0, 3};
+  int32_t pl[2] = {100, 0};
+  int64_t base[2] = {0, 200};
+  CHECK(st.check_prefill(1, 2, ids, pl, base, &err) == RSWA_E_STATE);  // not registered
+  CHECK(st.check_prefill(2, 2, ids, pl, base, &err) == RSWA_E_ARG);    // layer out of range
+  int32_t dup[2] = {1, 1};
+  CHECK(st.check_prefill(0, 2, dup, pl, base, &err) == RSWA_E_ARG);
+  int32_t badid[2] = {0, 4};
+  CHECK(st.check_prefill(0, 2, badid, pl, base, &err) == RSWA_E_ARG);
+  int32_t plbig[2] = {1001, 0};
+  CHECK(st.check_prefill(0, 2, ids, plbig, base, &err) == RSWA_E_POSITION);
+  int64_t basebig[2] = {0, 4000 - 8 + 1};
+  CHECK(st.check_prefill(0, 2, ids, pl, basebig, &err) == RSWA_E_CAPACITY);
+  int64_t baseedge[2] = {0, 4000 - 8};
+  CHECK(st.check_prefill(0, 2, ids, pl, baseedge, &err) == RSWA_OK);
+  int32_t plneg[2] = {-1, 0};
+  CHECK(st.check_prefill(0, 2, ids, plneg, base, &err) == RSWA_E_ARG);
+  // a failed check changed nothing
+  CHECK(st.request(0).plen == -1);
+
+  CHECK(st.check_prefill(0, 2, ids, pl, base, &err) == RSWA_OK);
+  st.commit_prefill(0, 2, ids, pl, base);
+  CHECK(st.request(0).plen == 100 && st.request(0).layers == 1 && st.request(0).t == 0);
+  int32_t pl2[2] = {101, 0};
+  CHECK(st.check_prefill(1, 2, ids, pl2, base, &err) == RSWA_E_STATE);  // P differs
+  CHECK(st.check_set_batch(2, ids, &err) == RSWA_E_STATE);              // layer 1 missing
+  CHECK(st.check_prefill(1, 2, ids, pl, base, &err) == RSWA_OK);
+  st.commit_prefill(1, 2, ids, pl, base);
+  CHECK(st.check_prefill(1, 2, ids, pl, base, &err) == RSWA_E_STATE);   // layer 1 again
+  CHECK(st.check_set_batch(2, ids, &err) == RSWA_OK);
+  // prefill plan: tiles cover each row once, longest first
+  PrefillPlan pp = st.plan_prefill(2, pl, 64);
+  CHECK(pp.total_tokens == 100 && pp.cu[1] == 100 && pp.cu[2] == 100);
+  CHECK(pp.num_tiles() == 2);
+  CHECK(pp.tiles[0] == 0 && pp.tiles[1] == 1 && pp.tiles[2] == 0 && pp.tiles[3] == 0);
+}
+
+static void register_all(HostState &st, int n, const int32_t *ids, const int32_t *pl,
+                         const int64_t *base) {
+  std::string err;
+  for (int l = 0; l < st.config().num_layers; ++l) {
+    CHECK(st.check_prefill(l, n, ids, pl, base, &err) == RSWA_OK);
+    st.commit_prefill(l, n, ids, pl, base);
+  }
+}
+
+static void test_step_machine_and_ring() {
+  rswa_config rc = base_cfg();
+  rc.max_positions = 120;
+  Config c = resolved(rc);
+  HostState st(c);
+  std::string err;
+  int32_t ids[2] = {2, 0};
+  int32_t pl[2] = {5, 100};
+  int64_t base[2] = {0, 50};
+  register_all(st, 2, ids, pl, base);
+  CHECK(st.check_ring_write(0, &err) == RSWA_E_STATE);  // no batch
+  CHECK(st.check_set_batch(2, ids, &err) == RSWA_OK);
+  st.commit_set_batch(2, ids, st.plan_decode(2, ids));
+  // in-batch requests cannot be re-prefilled
+  CHECK(st.check_prefill(0, 2, ids, pl, base, &err) == RSWA_E_STATE);
+
+  std::deque<int> fifo;  // generated indices resident in request 2's ring
+  for (int s = 0; s < 20; ++s) {
+    const RequestState &r = st.request(2);
+    // closed forms against a FIFO of generated tokens
+    CHECK(HostState::ring_pos(r.t, c.window) == s % c.window);
+    CHECK(HostState::next_pos(r.plen, r.t) == 5 + s);
+    CHECK(HostState::cache_len(r.plen, r.t, c.window) == 5 + (int)fifo.size());
+    CHECK(st.check_decode(0, &err) == RSWA_E_STATE);  // write first
+    CHECK(st.check_advance(&err) == RSWA_E_STATE);
+    CHECK(st.check_ring_write(0, &err) == RSWA_OK);
+    st.commit_ring_write(0);
+    CHECK(st.check_ring_write(0, &err) == RSWA_E_STATE);  // twice
+    CHECK(st.check_set_batch(2, ids, &err) == RSWA_E_STATE);  // mid-step
+    CHECK(st.check_decode(0, &err) == RSWA_OK);
+    st.commit_decode(0);
+    CHECK(st.check_decode(0, &err) == RSWA_E_STATE);
+    CHECK(st.check_advance(&err) == RSWA_E_STATE);  // layer 1 missing
+    CHECK(st.check_ring_write(1, &err) == RSWA_OK);
+    st.commit_ring_write(1);
+    CHECK(st.check_decode(1, &err) == RSWA_OK);
+    st.commit_decode(1);
+    CHECK(st.check_advance(&err) == RSWA_OK);
+    st.commit_advance();
+    fifo.push_back(s);
+    if ((int)fifo.size() > c.window) fifo.pop_front();
+  }
+  CHECK(st.request(2).t == 20 && st.request(0).t == 20);
+  CHECK(HostState::cache_len(5, 20, 8) == 13);
+  // request 0 (P = 100) reaches position 120 = max_positions after 20 steps
+  CHECK(st.check_ring_write(0, &err) == RSWA_E_POSITION);
+  CHECK(st.request(0).t == 20);
+}
+
+static void test_decode_plan() {
+  rswa_config rc = base_cfg();
+  rc.max_positions = 32768;
+  rc.max_requests = 64;
+  rc.num_slots = 64 * 40000;
+  rc.window = 128;
+  rc.max_prefill_tokens = 1 << 20;
+  Config c = resolved(rc);
+  HostState st(c);
+  std::vector<int32_t> ids(64), pl(64);
+  std::vector<int64_t> base(64);
+  int64_t b = 0;
+  for (int i = 0; i < 64; ++i) {
+    ids[i] = i;
+    pl[i] = 272 + (i * 7919) % 8000;
+    base[i] = b;
+    b += pl[i] + 128;
+  }
+  register_all(st, 64, ids.data(), pl.data(), base.data());
+  DecodePlan p = st.plan_decode(64, ids.data());
+  CHECK(p.split_tokens % 64 == 0 && p.split_tokens >= 64);
+  CHECK((int)p.split_off.size() == 65 && p.split_off[64] == p.num_splits());
+  for (int i = 0; i < 64; ++i) {
+    const int k = p.split_off[i + 1] - p.split_off[i];
+    // splits cover [0, P + W) exactly, the last one non-empty
+    CHECK((int64_t)k * p.split_tokens >= pl[i] + 128);
+    CHECK((int64_t)(k - 1) * p.split_tokens < pl[i] + 128);
+    for (int j = 0; j < k; ++j) {
+      CHECK(p.split_map[2 * (p.split_off[i] + j)] == i);
+      CHECK(p.split_map[2 * (p.split_off[i] + j) + 1] == j);
+    }
+  }
+  // forced split size; a too-small max_splits is reported
+  rc.decode_split_tokens = 64;
+  rc.max_splits = 100;
+  Config c2 = resolved(rc);
+  HostState st2(c2);
+  register_all(st2, 64, ids.data(), pl.data(), base.data());
+  std::string err;
+  CHECK(st2.check_set_batch(64, ids.data(), &err) == RSWA_E_CAPACITY);
+  rc.decode_split_tokens = 0;
+  Config c3 = resolved(rc);
+  HostState st3(c3);
+  register_all(st3, 64, ids.data(), pl.data(), base.data());
+  CHECK(st3.check_set_batch(64, ids.data(), &err) == RSWA_OK);
+  CHECK(st3.plan_decode(64, ids.data()).num_splits() <= 100);
+}
+
+int main() {
+  test_config();
+  test_layout();
+  test_prefill_order_and_errors();
+  test_step_machine_and_ring();
+  test_decode_plan();
+  if (g_fail) {
+    std::fprintf(stderr, "%d checks failed\n", g_fail);
+    return 1;
+  }
+  std::printf("host state: all checks passed\n");
+  return 0;
+}
