@@ -1,0 +1,389 @@
+"""R-SWA benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ragged_mix]
+
+One step is one whole job of the workload through the C ABI: causal prefill
+of every request in every layer (RoPE + cache write + attention), the
+staggered pre-roll that puts requests at different ring phases, then the
+measured decode steps (per layer: ring write + split-KV decode + combine;
+then advance).  Inputs are synthetic and already resident in HBM when timing
+starts.  Prints one JSON line.
+
+value = decode KV-read GB/s over the measured decode steps: per request,
+layer and step the method must read 4 * H * D * L bytes of bf16 keys and
+values, L = prefill_len + min(t + 1, W).  Prefill TFLOP/s counts
+4 * H * D * P (P + 1) / 2 per request and layer.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from kv_cache_management_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+METRIC = "R-SWA decode KV-read GB/s (% HBM peak), decode steps/s; prefill TFLOP/s"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_layer_step(w: W.Workload, t_before):
+    """Algorithmic K+V bytes one layer's decode reads for the active requests,
+    given each request's generated count before the step."""
+    eb = w.elem_bytes
+    return sum(2 * w.heads * w.head_dim * eb * (p + min(t + 1, w.window))
+               for p, t in zip(w.prefill_lens, t_before))
+
+
+def prefill_flops(w: W.Workload):
+    return sum(4 * w.heads * w.head_dim * p * (p + 1) // 2 for p in w.prefill_lens) * w.layers
+
+
+class Job:
+    """Device-resident inputs and the cache for one workload."""
+
+    def __init__(self, w: W.Workload, decode_steps: int, seed: int = 0):
+        import torch
+        from kv_cache_management_amd import rswa
+
+        self.torch = torch
+        self.R = rswa
+        self.lib = rswa.load()
+        self.w = w
+        self.steps = decode_steps
+        dev = torch.device("cuda", torch.cuda.current_device())
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        n, H, D, L = w.batch, w.heads, w.head_dim, w.layers
+        self.cache = rswa.RSWACache(L, H, D, w.window, max_requests=n, num_slots=w.pool_rows(),
+                                    dtype=w.dtype, max_positions=w.max_positions,
+                                    rope_base=w.rope_base, slot_table=w.slot_table(),
+                                    max_prefill_tokens=sum(w.prefill_lens))
+        self.h = self.cache.handle
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        total = sum(w.prefill_lens)
+
+        def rnd(shape):
+            t = torch.empty(shape, device=dev, dtype=tdt)
+            t.normal_(0.0, w.input_std, generator=gen)
+            return t
+
+        self.pf = [[rnd((total, H, D)) for _ in range(3)] for _ in range(L)]
+        self.pf_out = torch.empty((total, H, D), device=dev, dtype=tdt)
+        starts = w.starts()
+        self.pre = max(starts)
+        self.starts = starts
+        self.schedule = []
+        for g in range(self.pre):
+            act = [r for r in range(n) if starts[r] > self.pre - 1 - g]
+            self.schedule.append(act)
+        g_total = self.pre + decode_steps
+        log(f"allocating decode inputs: {g_total} steps x {L} layers x 3 x {n} x {H} x {D}")
+        self.dec = rnd((g_total, L, 3, n, H, D))
+        self.dec_out = torch.empty((L, n, H, D), device=dev, dtype=tdt)
+        # raw pointers for the hot loop
+        self.ids = np.arange(n, dtype=np.int32)
+        self.plen = np.array(w.prefill_lens, dtype=np.int32)
+        self.base = w.slot_bases().astype(np.int64)
+        self.c_ids = self.ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        self.c_plen = self.plen.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        self.c_base = self.base.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        row = n * H * D * self.dec.element_size()
+        self.dec_ptr0 = self.dec.data_ptr()
+        self.row_bytes = row
+        self.out_ptr = [self.dec_out[l].data_ptr() for l in range(L)]
+        self.stream = torch.cuda.current_stream(dev)
+        self.sptr = self.stream.cuda_stream
+        # measured-step KV bytes (all layers)
+        self.kv_bytes = 0
+        for s in range(decode_steps):
+            self.kv_bytes += L * kv_bytes_per_layer_step(w, [st + s for st in starts])
+        self.kv_launches = L * decode_steps
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        self.ev = {k: ev() for k in ("p0", "p1", "d0", "d1")}
+
+    def _check(self, st):
+        if st != 0:
+            raise self.R.RSWAError(st, self.R.rswa_last_error(self.h))
+
+    def _set_batch(self, act):
+        ids = np.array(act, dtype=np.int32)
+        self._check(self.lib.rswa_set_batch(self.h, len(ids),
+                                            ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                            self.sptr))
+
+    def _step(self, g, n_act):
+        lib, h, s = self.lib, self.h, self.sptr
+        L = self.w.layers
+        for l in range(L):
+            blk = self.dec_ptr0 + ((g * L + l) * 3) * self.row_bytes
+            q, k, v = blk, blk + self.row_bytes, blk + 2 * self.row_bytes
+            st = lib.rswa_ring_write(h, l, k, v, s)
+            if st:
+                self._check(st)
+            st = lib.rswa_decode_step(h, l, q, self.out_ptr[l], s)
+            if st:
+                self._check(st)
+        st = lib.rswa_advance(h, s)
+        if st:
+            self._check(st)
+
+    def run(self, profile_kernels: bool = False):
+        lib, h, s, w = self.lib, self.h, self.sptr, self.w
+        n = w.batch
+        self._set_batch([])
+        self.ev["p0"].record(self.stream)
+        lib.rswa_profile_enable(h, 1 if profile_kernels else 0)
+        for l in range(w.layers):
+            q, k, v = (t.data_ptr() for t in self.pf[l])
+            self._check(lib.rswa_prefill(h, l, n, self.c_ids, self.c_plen, self.c_base, q, k, v,
+                                         self.pf_out.data_ptr(), s))
+        lib.rswa_profile_enable(h, 0)
+        self.ev["p1"].record(self.stream)
+        current = None
+        for g, act in enumerate(self.schedule):
+            if act != current:
+                self._set_batch(act)
+                current = act
+            self._step(g, len(act))
+        if current != list(range(n)):
+            self._set_batch(list(range(n)))
+        self.ev["d0"].record(self.stream)
+        lib.rswa_profile_enable(h, 1 if profile_kernels else 0)
+        for i in range(self.steps):
+            self._step(self.pre + i, n)
+        lib.rswa_profile_enable(h, 0)
+        self.ev["d1"].record(self.stream)
+
+    def times_ms(self):
+        e = self.ev
+        e["d1"].synchronize()
+        return e["p0"].elapsed_time(e["p1"]), e["d0"].elapsed_time(e["d1"])
+
+    def kernel_time(self, kernel):
+        st, ms, cnt = self.R.rswa_profile_read(self.h, kernel, self.sptr)
+        self._check(st)
+        return ms, cnt
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per decode-split launch from the committed PMC summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"decode_split_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(ROOT, "kv_cache_management_amd", "csrc", "rswa_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    rec = None
+    for line in open(path):
+        if line.startswith("<!-- traffic "):
+            rec = json.loads(line[len("<!-- traffic "):].rsplit("-->", 1)[0])
+    if not rec or rec.get("kernel_source_sha256_16") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w: W.Workload, budget_s: float = 16.0):
+    """The oracle, as it stands, timed on this host's cores on a bounded sample
+    of the same workload (decode of sampled requests in steady state)."""
+    from kv_cache_management_amd import synth
+    from oracle import rswa_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = sum(i.get("num_threads", 0) for i in threadpool_info()
+                    if i.get("user_api") == "blas") or 1
+    except Exception:
+        cores = 1
+    n = w.batch
+    reqs = sorted(set(np.linspace(0, n - 1, min(8, n)).round().astype(int).tolist()))
+    starts = w.starts()
+    layer = 0
+    kv = 0
+    steps_done = 0
+    t_dec = 0.0
+    per_req_budget = budget_s * 0.75 / len(reqs)
+    for r in reqs:
+        p = w.prefill_lens[r]
+        pk = synth.draw(w.seed, w.wid, layer, synth.K_PREFILL, r, (p, w.heads, w.head_dim),
+                        w.input_std, w.dtype)
+        pv = synth.draw(w.seed, w.wid, layer, synth.V_PREFILL, r, (p, w.heads, w.head_dim),
+                        w.input_std, w.dtype)
+        rc = O.RingCache(p, w.window, w.heads, w.head_dim, w.rope_base)
+        rc.load_prefill(pk, pv)
+        s0 = starts[r] + w.window   # steady state: ring full
+        nmax = 64
+        dq, dk, dv = (synth.draw(w.seed, w.wid, layer, kind, r, (s0 + nmax, w.heads, w.head_dim),
+                                 w.input_std, w.dtype) for kind in (3, 4, 5))
+        for s in range(s0):           # fill the ring (untimed)
+            rc.write(dk[s], dv[s])
+            rc.s += 1
+        t0 = time.perf_counter()
+        for i in range(nmax):
+            s = s0 + i
+            rc.step(dq[s], dk[s], dv[s])
+            kv += 2 * w.heads * w.head_dim * w.elem_bytes * O.cache_len(p, s, w.window)
+            steps_done += 1
+            if time.perf_counter() - t0 > per_req_budget:
+                break
+        t_dec += time.perf_counter() - t0
+    # prefill: one request, full causal attention by definition
+    rp = reqs[len(reqs) // 2]
+    p = min(w.prefill_lens[rp], 2048)
+    q, k, v = (synth.draw(w.seed, w.wid, layer, kind, rp, (p, w.heads, w.head_dim),
+                          w.input_std, w.dtype) for kind in (0, 1, 2))
+    t0 = time.perf_counter()
+    O.prefill(q, k, v, w.rope_base)
+    t_pf = time.perf_counter() - t0
+    pf_flops = O.prefill_flops(p, w.heads, w.head_dim)
+    return {
+        "value": round(kv / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle (RingCache.step): {steps_done} steady-state decode steps of "
+                   f"requests {reqs} in layer {layer} ({kv / 1e9:.3f} GB of algorithmic KV reads "
+                   f"in {t_dec:.2f} s); prefill: one request, first {p} tokens, layer {layer}"),
+        "decode_steps_per_s_per_request_layer": round(steps_done / t_dec, 3),
+        "prefill_gflops": round(pf_flops / t_pf / 1e9, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="ragged_mix", choices=sorted(W.ALL))
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="measured decode steps per job (default: the workload's)")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="do not time kernels with event pairs inside the timed steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=16.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch) for counter calibration")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the R-SWA path here is single-GPU "
+              f"(requested --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(int(os.environ.get("LOCAL_RANK", "0")))
+    from kv_cache_management_amd import rswa
+
+    if args.copy_calibration:
+        # A plain copy kernel of known size: reads 1 GiB and writes 1 GiB.
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2,
+                          "launches": 3}))
+        return
+
+    w = W.ALL[args.workload]
+    steps = args.decode_steps or w.decode_steps
+    log(f"workload {w.name}: {w.batch} requests x {w.layers} layers, sum P = {sum(w.prefill_lens)}, "
+        f"{steps} decode steps")
+    job = Job(w, steps)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        t0 = time.perf_counter()
+        job.run(profile_kernels=False)
+        torch.cuda.synchronize()
+        log(f"warmup {i}: {time.perf_counter() - t0:.2f} s")
+    prof = not args.no_kernel_events
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pf_ms, dec_ms = [], []
+    for i in range(args.steps):
+        job.run(profile_kernels=prof)
+        a, b = job.times_ms()   # events of this step: synchronizes on them
+        pf_ms.append(a)
+        dec_ms.append(b)
+        log(f"step {i}: prefill {a:.2f} ms, decode {b:.2f} ms")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_dec = job.kernel_time(rswa.RSWA_KERNEL_DECODE_SPLIT) if prof else (None, 0)
+    k_pf = job.kernel_time(rswa.RSWA_KERNEL_PREFILL_ATTENTION) if prof else (None, 0)
+
+    dec_s = sum(dec_ms) / 1e3
+    kv_total = job.kv_bytes * args.steps
+    value = kv_total / dec_s / 1e9
+    pf_flops = prefill_flops(w)
+    pf_tflops = pf_flops * args.steps / (sum(pf_ms) / 1e3) / 1e12
+    roofline = None
+    if prof and k_dec[1]:
+        per_launch_bytes = job.kv_bytes / job.kv_launches
+        avg_s = k_dec[0] / k_dec[1] / 1e3
+        achieved = per_launch_bytes / avg_s / 1e9
+        traffic = traffic_from_profile(w.name)
+        roofline = {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic,
+                    "algorithmic_bytes_per_launch": int(per_launch_bytes),
+                    "avg_launch_us": round(avg_s * 1e6, 2), "launches": k_dec[1]}
+    prefill_kernel = None
+    if prof and k_pf[1]:
+        avg_s = k_pf[0] / k_pf[1] / 1e3
+        per_launch = pf_flops / w.layers
+        prefill_kernel = {"bound": "mfma", "achieved": round(per_launch / avg_s / 1e12, 2),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(per_launch / avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "avg_launch_us": round(avg_s * 1e6, 1), "launches": k_pf[1]}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.batch, "layers": w.layers, "heads": w.heads,
+                   "head_dim": w.head_dim, "window": w.window, "decode_steps": steps,
+                   "prefill_tokens": sum(w.prefill_lens),
+                   "kv_layout": "page-size-1 slot table" if w.paged else "contiguous"},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "decode_steps_per_s": round(steps * args.steps / dec_s, 2),
+        "decode_ms_per_step": round(dec_s * 1e3 / (steps * args.steps), 4),
+        "prefill_tflops": round(pf_tflops, 2),
+        "prefill_mfma_frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline,
+        "prefill_kernel": prefill_kernel,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    job.cache.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

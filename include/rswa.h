@@ -172,6 +172,17 @@ int rswa_get_state(rswa_cache *c, int32_t n, const int32_t *req_ids,
  * items planned for the current batch; 0s before rswa_set_batch. */
 int rswa_decode_plan(const rswa_cache *c, int32_t *split_tokens, int32_t *num_splits);
 
+/* Kernel timing, for measurement.  While enabled, the library records a HIP
+ * event pair on the caller's stream immediately before and after every launch
+ * of the selected kernels.  rswa_profile_read synchronizes `stream`, returns
+ * the summed elapsed milliseconds and the launch count of one kernel since
+ * the last read, and resets that kernel's record.  Off by default; enabling
+ * it costs two event records per timed launch. */
+enum { RSWA_KERNEL_DECODE_SPLIT = 0, RSWA_KERNEL_PREFILL_ATTENTION = 1, RSWA_NUM_KERNELS = 2 };
+int rswa_profile_enable(rswa_cache *c, int enable);
+int rswa_profile_read(rswa_cache *c, int32_t kernel, double *total_ms, int64_t *launches,
+                      void *stream);
+
 /* Static name of a status code. */
 const char *rswa_status_string(int status);
 

@@ -76,7 +76,8 @@ struct PrefillArgs {
 // dtype: RSWA_DTYPE_BF16 or RSWA_DTYPE_F32; head_dim 64 or 128.
 hipError_t launch_ring_write(const RingWriteArgs &a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_advance(const AdvanceArgs &a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_decode_split(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_decode_combine(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
 // Query-tile height the prefill attention kernel for (dtype, head_dim) uses.

@@ -82,6 +82,32 @@ struct rswa_cache {
   const float2 *rope() const { return (const float2 *)(ws + lay.rope); }
 
   const int32_t *slot_table = nullptr;
+
+  // Kernel timing (rswa_profile_*): event pairs per kernel kind, reused.
+  bool prof = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[RSWA_NUM_KERNELS];
+  size_t prof_used[RSWA_NUM_KERNELS] = {};
+
+  // Records the opening event of a timed launch; returns the pair index or -1.
+  int prof_begin(int kernel, hipStream_t s) {
+    if (!prof) return -1;
+    auto &v = prof_ev[kernel];
+    if (prof_used[kernel] == v.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return -1;
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return -1;
+      }
+      v.emplace_back(a, b);
+    }
+    const int i = (int)prof_used[kernel]++;
+    (void)hipEventRecord(v[i].first, s);
+    return i;
+  }
+  void prof_end(int kernel, int i, hipStream_t s) {
+    if (i >= 0) (void)hipEventRecord(prof_ev[kernel][i].second, s);
+  }
 };
 
 namespace {
@@ -220,6 +246,12 @@ int rswa_cache_init(const rswa_config *cfg, void *k_pool, void *v_pool, void *wo
 
 int rswa_cache_destroy(rswa_cache *c) {
   if (!c) return RSWA_OK;
+  for (auto &v : c->prof_ev)
+    for (auto &pr : v) {
+      (void)hipEventSynchronize(pr.second);
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
   for (int k = 0; k < kStages; ++k) {
     if (c->staged[k]) {
       if (c->staged_live[k]) (void)hipEventSynchronize(c->staged[k]);
@@ -286,7 +318,9 @@ int rswa_prefill(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids
     }
     e = rswa::launch_prefill_cache_write(a, cf.dtype, cf.head_dim, s);
     if (e != hipSuccess) return c->hip_fail(e, "prefill cache write launch");
+    const int pi = c->prof_begin(RSWA_KERNEL_PREFILL_ATTENTION, s);
     e = rswa::launch_prefill_attention(a, cf.dtype, cf.head_dim, s);
+    c->prof_end(RSWA_KERNEL_PREFILL_ATTENTION, pi, s);
     if (e != hipSuccess) return c->hip_fail(e, "prefill attention launch");
     c->st.commit_prefill(layer, n, req_ids, prefill_len, slot_base);
     return RSWA_OK;
@@ -373,8 +407,13 @@ int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out, voi
     a.layer = layer;
     a.num_splits = plan.num_splits();
     a.split_tokens = plan.split_tokens;
-    hipError_t e = rswa::launch_decode(a, c->cfg.dtype, c->cfg.head_dim, (hipStream_t)stream);
-    if (e != hipSuccess) return c->hip_fail(e, "decode launch");
+    hipStream_t s = (hipStream_t)stream;
+    const int pi = c->prof_begin(RSWA_KERNEL_DECODE_SPLIT, s);
+    hipError_t e = rswa::launch_decode_split(a, c->cfg.dtype, c->cfg.head_dim, s);
+    c->prof_end(RSWA_KERNEL_DECODE_SPLIT, pi, s);
+    if (e != hipSuccess) return c->hip_fail(e, "split-KV decode launch");
+    e = rswa::launch_decode_combine(a, c->cfg.dtype, c->cfg.head_dim, s);
+    if (e != hipSuccess) return c->hip_fail(e, "decode combine launch");
     c->st.commit_decode(layer);
     return RSWA_OK;
   });
@@ -437,6 +476,32 @@ int rswa_decode_plan(const rswa_cache *c, int32_t *split_tokens, int32_t *num_sp
   if (!c) return set_global_error(RSWA_E_ARG, "null handle");
   if (split_tokens) *split_tokens = c->st.plan().split_tokens;
   if (num_splits) *num_splits = c->st.plan().num_splits();
+  return RSWA_OK;
+}
+
+int rswa_profile_enable(rswa_cache *c, int enable) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  c->prof = enable != 0;
+  return RSWA_OK;
+}
+
+int rswa_profile_read(rswa_cache *c, int32_t kernel, double *total_ms, int64_t *launches,
+                      void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  if (kernel < 0 || kernel >= RSWA_NUM_KERNELS) return c->fail(RSWA_E_ARG, "unknown kernel id");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return c->hip_fail(e, "profile read");
+  double sum = 0;
+  auto &v = c->prof_ev[kernel];
+  for (size_t i = 0; i < c->prof_used[kernel]; ++i) {
+    float ms = 0;
+    e = hipEventElapsedTime(&ms, v[i].first, v[i].second);
+    if (e != hipSuccess) return c->hip_fail(e, "hipEventElapsedTime");
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = (int64_t)c->prof_used[kernel];
+  c->prof_used[kernel] = 0;
   return RSWA_OK;
 }
 

@@ -444,7 +444,7 @@ hipError_t launch_advance(const AdvanceArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s) {
+hipError_t launch_decode_split(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
     using T = decltype(tv);
@@ -455,8 +455,15 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream
       hipLaunchKernelGGL((decode_split_kernel<T, D, true>), grid, dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((decode_split_kernel<T, D, false>), grid, dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_decode_combine(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
+    using T = decltype(tv);
+    constexpr int D = decltype(dv)::value;
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.n * a.heads), dim3(64), 0, s, a);
     return hipGetLastError();
   });

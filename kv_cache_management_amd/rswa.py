@@ -34,8 +34,10 @@ EXPORTED = (
     "rswa_abi_version", "rswa_workspace_bytes", "rswa_cache_init", "rswa_cache_destroy",
     "rswa_prefill", "rswa_set_batch", "rswa_ring_write", "rswa_decode_step",
     "rswa_advance", "rswa_get_state", "rswa_decode_plan", "rswa_status_string",
-    "rswa_last_error",
+    "rswa_last_error", "rswa_profile_enable", "rswa_profile_read",
 )
+RSWA_KERNEL_DECODE_SPLIT = 0
+RSWA_KERNEL_PREFILL_ATTENTION = 1
 
 
 class rswa_config(ctypes.Structure):
@@ -114,6 +116,9 @@ def load():
         "rswa_decode_plan": (ctypes.c_int, [P, pI32, pI32]),
         "rswa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "rswa_last_error": (ctypes.c_char_p, [P]),
+        "rswa_profile_enable": (ctypes.c_int, [P, ctypes.c_int]),
+        "rswa_profile_read": (ctypes.c_int, [P, I32, ctypes.POINTER(ctypes.c_double),
+                                             ctypes.POINTER(ctypes.c_int64), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -201,6 +206,18 @@ def rswa_decode_plan(handle):
     k = ctypes.c_int32()
     st = load().rswa_decode_plan(handle, ctypes.byref(s), ctypes.byref(k))
     return st, s.value, k.value
+
+
+def rswa_profile_enable(handle, enable: bool) -> int:
+    return load().rswa_profile_enable(handle, 1 if enable else 0)
+
+
+def rswa_profile_read(handle, kernel: int, stream: int):
+    """Returns (status, total_ms, launches)."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    st = load().rswa_profile_read(handle, kernel, ctypes.byref(ms), ctypes.byref(n), stream)
+    return st, ms.value, n.value
 
 
 def rswa_status_string(status: int) -> str:
