@@ -66,6 +66,15 @@ int resolve_config(const rswa_config &in, Config *out, std::string *err) {
     return fail(err, RSWA_E_ARG, "rope_base must be positive");
   if (!std::isfinite(in.softmax_scale)) return fail(err, RSWA_E_ARG, "softmax_scale must be finite");
   if (c.softmax_scale == 0) c.softmax_scale = 1.0 / std::sqrt((double)c.head_dim);
+  // Decode addresses a request's rows (and, with a slot table, a whole layer)
+  // through 32-bit buffer offsets.
+  const int64_t row_bytes = (int64_t)c.num_heads * c.head_dim * c.elem_bytes();
+  if (((int64_t)c.max_positions + c.window) * row_bytes > (int64_t)UINT32_MAX)
+    return fail(err, RSWA_E_UNSUPPORTED, "(max_positions + window) * heads * head_dim * elem_bytes "
+                                         "must be < 2^32");
+  if (c.has_table && c.num_slots * row_bytes > (int64_t)UINT32_MAX)
+    return fail(err, RSWA_E_UNSUPPORTED, "with a slot table, one layer of a pool "
+                                         "(num_slots * heads * head_dim * elem_bytes) must be < 2^32 bytes");
   if (c.has_table) {
     if (c.slot_table_len < 1 || c.slot_table_len > INT32_MAX)
       return fail(err, RSWA_E_ARG, "slot_table_len must be in [1, 2^31-1] with a slot table");

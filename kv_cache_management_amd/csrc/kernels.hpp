@@ -52,6 +52,7 @@ struct DecodeArgs {
   float2 *part_ml;            // [num_splits][H]  (running max in log2 units, sum)
   const float2 *rope;
   float qscale;               // softmax_scale * log2(e)
+  uint32_t layer_bytes;       // bytes of one layer of a pool (< 2^32)
   int32_t n, heads, window, layer, num_splits, split_tokens;
 };
 

@@ -401,6 +401,8 @@ int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out, voi
     a.part_ml = (float2 *)(c->ws + c->lay.part_ml);
     a.rope = c->rope();
     a.qscale = c->qscale;
+    a.layer_bytes = (uint32_t)(c->cfg.num_slots * c->cfg.num_heads * c->cfg.head_dim *
+                               c->cfg.elem_bytes());
     a.n = n;
     a.heads = c->cfg.num_heads;
     a.window = c->cfg.window;

@@ -1,8 +1,7 @@
-// gfx950 kernels of the R-SWA hot path, except the MFMA prefill attention:
-// ring write (RoPE at the absolute position, in-place slot overwrite),
-// split-KV flash-decode over the frozen prefill plus the ring, the
-// cross-split combine, the step advance, and prefill registration / cache
-// write / a VALU causal attention used for fp32 and as a reference path.
+// gfx950 kernels of the R-SWA hot path other than decode attention and the
+// MFMA prefill attention: ring write (RoPE at the absolute position, in-place
+// slot overwrite), the step advance, prefill registration and cache write,
+// and a VALU causal prefill attention used for fp32 and as a reference path.
 //
 // The cache policy is that of page "开源5天Star破万之后：百度Unlimited-OCR的爆火
 // 路径复盘" (www.gtnt.cn/news/146005), section 2.1: prefill rows are kept
@@ -14,60 +13,14 @@
 
 #include <cmath>
 
+#include "device_common.hpp"
 #include "kernels.hpp"
 #include "rswa.h"
 
 namespace rswa {
 namespace {
 
-using bf16 = __bf16;
-
-__device__ __forceinline__ float to_f(float x) { return x; }
-__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
-template <typename T> __device__ __forceinline__ T from_f(float x);
-template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
-template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
-
-// A 16-byte vector of T unpacked to fp32.
-template <typename T> struct Vec16;
-template <> struct Vec16<float> {
-  static constexpr int N = 4;
-  static __device__ __forceinline__ void unpack(const uint4 &u, float *f) {
-    f[0] = __uint_as_float(u.x);
-    f[1] = __uint_as_float(u.y);
-    f[2] = __uint_as_float(u.z);
-    f[3] = __uint_as_float(u.w);
-  }
-};
-template <> struct Vec16<bf16> {
-  static constexpr int N = 8;
-  static __device__ __forceinline__ void unpack(const uint4 &u, float *f) {
-    f[0] = __uint_as_float(u.x << 16);
-    f[1] = __uint_as_float(u.x & 0xffff0000u);
-    f[2] = __uint_as_float(u.y << 16);
-    f[3] = __uint_as_float(u.y & 0xffff0000u);
-    f[4] = __uint_as_float(u.z << 16);
-    f[5] = __uint_as_float(u.z & 0xffff0000u);
-    f[6] = __uint_as_float(u.w << 16);
-    f[7] = __uint_as_float(u.w & 0xffff0000u);
-  }
-};
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
-__device__ __forceinline__ int64_t pool_row(const int32_t *table, int64_t base, int64_t i) {
-  return table ? (int64_t)table[base + i] : base + i;
-}
+using namespace dev;
 
 // ---------------------------------------------------------------------------
 // Ring write: one block of 64 threads per (batch entry, head).
@@ -106,191 +59,6 @@ __global__ __launch_bounds__(64) void ring_write_kernel(RingWriteArgs a) {
 __global__ __launch_bounds__(256) void advance_kernel(AdvanceArgs a) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b < a.n) a.st.t[a.batch_req[b]] += 1;
-}
-
-// ---------------------------------------------------------------------------
-// Split-KV decode.  One wavefront per (split work item, head); four
-// independent wavefronts per block.  A split covers keys
-// [s * split_tokens, min((s+1) * split_tokens, L)) of logical slots
-// 0 .. L-1, L = P + min(t + 1, W).
-//
-// Keys are streamed 64 at a time.  A head's key row is D * sizeof(T) bytes =
-// LPR lanes x 16 bytes, so one 16-byte load per lane covers TPI = 64 / LPR
-// rows and NI = LPR loads cover the 64-key chunk.  Lane (g, c) = (lane / LPR,
-// lane % LPR) multiplies its 16-byte slice of row i * TPI + g with the
-// matching query slice; a reduce-scatter over the LPR lanes of a row group
-// then leaves lane (g, c) with the full score of key c * TPI + g.  Softmax
-// runs online in base 2 (the query carries scale * log2 e).  The
-// probabilities go through LDS so each lane can weight the value slices it
-// loaded with the same row mapping.  Per split the wave writes its running
-// max, sum and unnormalised output vector.
-// ---------------------------------------------------------------------------
-template <typename T, int D, bool PAGED>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  constexpr int EPL = Vec16<T>::N;  // elements per 16-byte load
-  constexpr int LPR = D / EPL;      // lanes per key row
-  constexpr int TPI = 64 / LPR;     // key rows per load instruction
-  constexpr int NI = LPR;           // load instructions per 64-key chunk
-  static_assert(TPI * NI == 64, "chunk must be 64 keys");
-  __shared__ float lds_p[4][64];
-  __shared__ int32_t lds_row[4][64];
-
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int task = blockIdx.x * 4 + wid;
-  if (task >= a.num_splits * a.heads) return;
-  const int ks = task / a.heads;
-  const int h = task % a.heads;
-  const int b = a.split_map[2 * ks];
-  const int s = a.split_map[2 * ks + 1];
-  const int r = a.batch_req[b];
-  const int p_len = a.st.plen[r];
-  const int t = a.st.t[r];
-  const int64_t base = a.st.base[r];
-  const int L = p_len + min(t + 1, a.window);
-  const int start = s * a.split_tokens;
-  float2 *ml = a.part_ml + (int64_t)ks * a.heads + h;
-  if (start >= L) {
-    if (lane == 0) *ml = make_float2(-INFINITY, 0.f);
-    return;
-  }
-  const int end = min(start + a.split_tokens, L);
-  const int g = lane / LPR;
-  const int c = lane % LPR;
-
-  // Query rotated at position P + t, pre-scaled by scale * log2(e).
-  const int pos = p_len + t;
-  const T *qp = (const T *)a.q + ((int64_t)b * a.heads + h) * D;
-  const float2 *cs = a.rope + (int64_t)pos * (D / 2);
-  float qh[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int d = c * EPL + e;
-    const float x = to_f(qp[d]);
-    const float y = d < D / 2 ? -to_f(qp[d + D / 2]) : to_f(qp[d - D / 2]);
-    const float2 cc = cs[d % (D / 2)];
-    qh[e] = (x * cc.x + y * cc.y) * a.qscale;
-  }
-
-  const int64_t row_stride = (int64_t)a.heads * D;
-  const T *Kl = (const T *)a.pool.k + (int64_t)a.layer * a.pool.layer_stride + h * D + c * EPL;
-  const T *Vl = (const T *)a.pool.v + (int64_t)a.layer * a.pool.layer_stride + h * D + c * EPL;
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  float o[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-
-  for (int c0 = start; c0 < end; c0 += 64) {
-    int64_t rows[NI];
-    if (PAGED) {
-      // Row of chunk key `lane`, stored so that lane (g, c) finds the rows of
-      // keys i * TPI + g (i = 0 .. NI-1) contiguously at [g * NI + i].
-      const int jj = min(c0 + lane, end - 1);
-      lds_row[wid][(lane % TPI) * NI + lane / TPI] = a.pool.table[base + jj];
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int i = 0; i < NI; ++i) rows[i] = lds_row[wid][g * NI + i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) rows[i] = base + min(c0 + i * TPI + g, end - 1);
-    }
-    uint4 kr[NI], vr[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) kr[i] = *(const uint4 *)(Kl + rows[i] * row_stride);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = *(const uint4 *)(Vl + rows[i] * row_stride);
-
-    float sc[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float kf[EPL];
-      Vec16<T>::unpack(kr[i], kf);
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc = fmaf(qh[e], kf[e], acc);
-      sc[i] = acc;
-    }
-    // Reduce-scatter across the LPR lanes of the row group: after the stage
-    // with mask m each lane keeps the half of the live values selected by
-    // bit m of c and adds its partner's copy of that half.
-#pragma unroll
-    for (int m = NI / 2; m >= 1; m >>= 1) {
-      const bool up = (c & m) != 0;
-#pragma unroll
-      for (int k = 0; k < m; ++k) {
-        const float keep = up ? sc[k + m] : sc[k];
-        const float send = up ? sc[k] : sc[k + m];
-        sc[k] = keep + __shfl_xor(send, m);
-      }
-    }
-    float score = sc[0];  // key c0 + c * TPI + g
-    if (c0 + c * TPI + g >= end) score = -INFINITY;
-    const float m_new = fmaxf(m_run, wave_max(score));
-    const float alpha = exp2f(m_run - m_new);
-    const float p = exp2f(score - m_new);
-    l_run = l_run * alpha + p;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] *= alpha;
-    m_run = m_new;
-
-    // Key i * TPI + g is owned by lane g * LPR + i.
-    lds_p[wid][lane] = p;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float pi = lds_p[wid][g * LPR + i];
-      float vf[EPL];
-      Vec16<T>::unpack(vr[i], vf);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pi, vf[e], o[e]);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  const float l_tot = wave_sum(l_run);
-#pragma unroll
-  for (int msk = LPR; msk < 64; msk <<= 1) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], msk);
-  }
-  if (g == 0) {
-    float *po = a.part_o + ((int64_t)ks * a.heads + h) * D + c * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; e += 4) *(float4 *)(po + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-  }
-  if (lane == 0) *ml = make_float2(m_run, l_tot);
-}
-
-// Cross-split combine: one wavefront per (batch entry, head).
-// M = max_s m_s; out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-  const int b = blockIdx.x / a.heads;
-  const int h = blockIdx.x % a.heads;
-  const int k0 = a.split_off[b];
-  const int k1 = a.split_off[b + 1];
-  const int lane = threadIdx.x;
-  float mx = -INFINITY;
-  for (int k = k0; k < k1; ++k) mx = fmaxf(mx, a.part_ml[(int64_t)k * a.heads + h].x);
-  float den = 0.f;
-  float acc[D / 64];
-#pragma unroll
-  for (int j = 0; j < D / 64; ++j) acc[j] = 0.f;
-  for (int k = k0; k < k1; ++k) {
-    const float2 m_l = a.part_ml[(int64_t)k * a.heads + h];
-    if (m_l.y == 0.f) continue;  // split past the cache end: no keys
-    const float w = exp2f(m_l.x - mx);
-    den += w * m_l.y;
-    const float *po = a.part_o + ((int64_t)k * a.heads + h) * D;
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) acc[j] = fmaf(w, po[lane + 64 * j], acc[j]);
-  }
-  T *out = (T *)a.out + ((int64_t)b * a.heads + h) * D;
-  const float inv = 1.f / den;
-#pragma unroll
-  for (int j = 0; j < D / 64; ++j) out[lane + 64 * j] = from_f<T>(acc[j] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -442,31 +210,6 @@ hipError_t launch_advance(const AdvanceArgs &a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   hipLaunchKernelGGL(advance_kernel, dim3((a.n + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
-}
-
-hipError_t launch_decode_split(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
-  return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
-    using T = decltype(tv);
-    constexpr int D = decltype(dv)::value;
-    const int64_t tasks = (int64_t)a.num_splits * a.heads;
-    const dim3 grid((unsigned)((tasks + 3) / 4));
-    if (a.pool.table)
-      hipLaunchKernelGGL((decode_split_kernel<T, D, true>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<T, D, false>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-  });
-}
-
-hipError_t launch_decode_combine(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
-  return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
-    using T = decltype(tv);
-    constexpr int D = decltype(dv)::value;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.n * a.heads), dim3(64), 0, s, a);
-    return hipGetLastError();
-  });
 }
 
 hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s) {
