@@ -81,6 +81,9 @@ hipError_t launch_decode_split(const DecodeArgs &a, int dtype, int head_dim, hip
 hipError_t launch_decode_combine(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
+// bf16 MFMA causal prefill attention (128-row query tiles).
+bool prefill_mfma_supported(int dtype, int head_dim);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, int head_dim, hipStream_t s);
 // Query-tile height the prefill attention kernel for (dtype, head_dim) uses.
 int prefill_tile_rows(int dtype, int head_dim);
 hipError_t launch_prefill_attention(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);

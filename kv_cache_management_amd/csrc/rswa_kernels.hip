@@ -228,10 +228,13 @@ hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_
   });
 }
 
-int prefill_tile_rows(int dtype, int head_dim) { return 64; }
+int prefill_tile_rows(int dtype, int head_dim) {
+  return prefill_mfma_supported(dtype, head_dim) ? 128 : 64;
+}
 
 hipError_t launch_prefill_attention(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s) {
   if (a.num_tiles == 0) return hipSuccess;
+  if (prefill_mfma_supported(dtype, head_dim)) return launch_prefill_mfma(a, head_dim, s);
   return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
     using T = decltype(tv);
     constexpr int D = decltype(dv)::value;

@@ -1,0 +1,263 @@
+// Causal prefill attention on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+//
+// The prefill segment keeps complete attention and loses no token (page
+// "开源5天Star破万之后：百度Unlimited-OCR的爆火路径复盘", www.gtnt.cn/news/146005,
+// section 2.1); the page's eager path computes it with a full-matrix softmax
+// (section 三).  Here it is a flash-attention forward: one block per (query
+// tile of 128 rows, head, request), 4 wavefronts of 32 query rows each, key
+// tiles of 64 streamed through LDS, online softmax in base 2.
+//
+// Per wavefront and key tile:
+//   S^T (64 keys x 32 queries) = K (64 x D) . Q^T (D x 32): A = K rows from
+//     LDS, B = the wave's rotated queries held in registers.  In the result
+//     layout each lane owns one query column, so row max / sum are in-lane
+//     plus one exchange with lane ^ 32.
+//   O^T (D x 32) += V^T (D x 64) . P^T (64 x 32): B = the probabilities,
+//     straight from the S^T registers (converted to bf16), A = V^T read from
+//     an LDS tile stored transposed.  The key order inside each 16-key MFMA
+//     step follows the S^T register layout; V^T is read in the same order.
+// Keys come from the pool (already rotated by the cache write); queries are
+// rotated on load at their absolute positions.  Probabilities are rounded to
+// bf16 for the P.V product; accumulation is fp32.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "rswa.h"
+
+namespace rswa {
+namespace {
+
+using namespace dev;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128;  // query rows per block
+constexpr int kBN = 64;   // keys per tile
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
+  constexpr int KP = D + 8;        // K tile row stride in LDS (elements)
+  constexpr int VP = kBN + 8;      // V^T tile row stride in LDS (elements)
+  constexpr int DB = D / 32;       // 32-dim blocks of the output
+  constexpr int CPR = D / 8;       // 16-byte chunks per key row
+  constexpr int KLD = kBN * CPR / 256;        // K chunks per thread per tile
+  constexpr int VLD = (kBN / 4) * CPR;        // V (4-key x 8-dim) items per tile
+  static_assert(KLD >= 1 && kBN * CPR % 256 == 0, "tile must split evenly");
+  __shared__ __attribute__((aligned(16))) bf16 lk[kBN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 lv[D * VP];
+
+  const int item = blockIdx.x / a.heads;
+  const int h = blockIdx.x % a.heads;
+  const int b = a.tiles[2 * item];
+  const int qt = a.tiles[2 * item + 1];
+  const int p_len = a.plen[b];
+  const int64_t base = a.base[b];
+  const int64_t cu = a.cu[b];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;
+  const int q0 = qt * kBM + w * 32;   // first query row of this wave
+  const int qi = q0 + (lane & 31);    // query row of this lane
+  const int row_stride = a.heads * D;
+  const bf16 *Kp = (const bf16 *)a.pool.k + (int64_t)a.layer * a.pool.layer_stride + h * D;
+  const bf16 *Vp = (const bf16 *)a.pool.v + (int64_t)a.layer * a.pool.layer_stride + h * D;
+  const int32_t *table = a.pool.table;
+
+  // ---- queries: B operand fragments, rotated at their positions ----------
+  bf16x8 qf[KS];
+  {
+    float qv[KS][8];
+    const bool qok = qi < p_len;
+    const bf16 *qp = (const bf16 *)a.q + ((cu + (qok ? qi : 0)) * a.heads + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 u = qok ? *(const uint4 *)(qp + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+      Vec16<bf16>::unpack(u, qv[ks]);
+    }
+    const float2 *cs = a.rope + (int64_t)(qok ? qi : 0) * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 c = cs[16 * ks + 8 * g + e];
+        const float x1 = qv[ks][e];
+        const float x2 = qv[ks + KS / 2][e];
+        qf[ks][e] = (bf16)(x1 * c.x - x2 * c.y);
+        qf[ks + KS / 2][e] = (bf16)(x2 * c.x + x1 * c.y);
+      }
+    }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float qscale = a.qscale;
+
+  const int kend = min(p_len, qt * kBM + kBM);
+  const int ntile = (kend + kBN - 1) / kBN;
+
+  // ---- tile loads: global -> registers -> LDS -----------------------------
+  uint4 kreg[KLD];
+  uint4 vreg[4];
+  const int vkq = tid % (kBN / 4);   // key quad of this thread's V item
+  const int vch = tid / (kBN / 4);   // 8-dim chunk of this thread's V item
+  auto row_of = [&](int j) -> int64_t {
+    return table ? (int64_t)table[base + j] : base + j;
+  };
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < KLD; ++it) {
+      const int idx = tid + 256 * it;
+      const int j = k0 + idx / CPR;
+      kreg[it] = j < kend ? *(const uint4 *)(Kp + row_of(j) * row_stride + (idx % CPR) * 8)
+                          : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < VLD) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = k0 + 4 * vkq + r;
+        vreg[r] = j < kend ? *(const uint4 *)(Vp + row_of(j) * row_stride + vch * 8)
+                           : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < KLD; ++it) {
+      const int idx = tid + 256 * it;
+      *(uint4 *)(lk + (idx / CPR) * KP + (idx % CPR) * 8) = kreg[it];
+    }
+    if (tid < VLD) {
+      // Transpose 4 keys x 8 dims: dim e of keys 4kq..4kq+3 -> one 8-byte row piece.
+      const uint32_t *v0 = (const uint32_t *)&vreg[0];
+      const uint32_t *v1 = (const uint32_t *)&vreg[1];
+      const uint32_t *v2 = (const uint32_t *)&vreg[2];
+      const uint32_t *v3 = (const uint32_t *)&vreg[3];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        const uint32_t a0 = (v0[e >> 1] >> sh) & 0xffffu, a1 = (v1[e >> 1] >> sh) & 0xffffu;
+        const uint32_t a2 = (v2[e >> 1] >> sh) & 0xffffu, a3 = (v3[e >> 1] >> sh) & 0xffffu;
+        uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+        *(uint2 *)(lv + (vch * 8 + e) * VP + 4 * vkq) = pk;
+      }
+    }
+  };
+
+  if (ntile > 0) load_tile(0);
+  for (int kt = 0; kt < ntile; ++kt) {
+    const int k0 = kt * kBN;
+    __syncthreads();  // every wave is done reading the previous tile
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < ntile) load_tile(k0 + kBN);
+    if (k0 > q0 + 31) continue;  // tile entirely above this wave's diagonal
+
+    // S^T = K . Q^T, two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[j][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = *(const bf16x8 *)(lk + (32 * j + (lane & 31)) * KP + 16 * ks + 8 * g);
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[j], 0, 0, 0);
+      }
+    }
+    // causal mask (key > query) on tiles that reach the diagonal
+    if (k0 + kBN - 1 > q0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key > qi) s[j][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * qscale);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float lsum = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][r], qscale, -m_new));
+        lsum += p;
+        pf[j][r >> 3][r & 7] = (bf16)p;
+      }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const bf16 *vrow = lv + (32 * d + (lane & 31)) * VP + 4 * g;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x4 lo = *(const bf16x4 *)(vrow + 32 * j + 16 * hh);
+          const bf16x4 hi = *(const bf16x4 *)(vrow + 32 * j + 16 * hh + 8);
+          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[j][hh], o[d], 0, 0, 0);
+        }
+    }
+  }
+
+  if (qi >= p_len) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.f / l_tot;
+  bf16 *op = (bf16 *)a.out + ((cu + qi) * a.heads + h) * D;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[d][4 * q4 + e] * inv);
+      *(bf16x4 *)(op + 32 * d + 8 * q4 + 4 * g) = v;
+    }
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(int dtype, int head_dim) {
+  return dtype == RSWA_DTYPE_BF16 && (head_dim == 64 || head_dim == 128);
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs &a, int head_dim, hipStream_t s) {
+  if (a.num_tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.num_tiles * a.heads));
+  if (head_dim == 128)
+    hipLaunchKernelGGL((prefill_mfma_kernel<128>), grid, dim3(256), 0, s, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((prefill_mfma_kernel<64>), grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace rswa
