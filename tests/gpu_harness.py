@@ -65,6 +65,9 @@ class Scenario:
     prefill_rows: Optional[Sequence[int]] = None     # None: all rows
     split_tokens: int = 0
     poison: bool = True
+    # Fill (layer, request) slices that are not checked with device-side
+    # normals of the same distribution instead of host-drawn inputs.
+    device_fill: bool = False
 
 
 class Inputs:
@@ -114,11 +117,29 @@ def run_gpu(sc: Scenario, inputs: Inputs, record_state: bool = True):
                       pool_fill=float("nan") if sc.poison else None)
     ids = list(range(n))
     res = {"prefill": {}, "decode": {}, "state": [], "cache": cache}
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    offs = np.concatenate([[0], np.cumsum(w.prefill_lens)]).astype(np.int64)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234 + w.wid)
+
+    def filled(shape):
+        return torch.empty(shape, device="cuda", dtype=tdt).normal_(0.0, w.input_std, generator=gen)
+
+    def checked(l, r):
+        return l in check_layers and r in check_reqs
+
     for l in layers:
-        q = np.concatenate([inputs.prefill(l, synth.Q_PREFILL, r) for r in ids])
-        k = np.concatenate([inputs.prefill(l, synth.K_PREFILL, r) for r in ids])
-        v = np.concatenate([inputs.prefill(l, synth.V_PREFILL, r) for r in ids])
-        tq, tk, tv = (to_torch(x, w.dtype) for x in (q, k, v))
+        if sc.device_fill:
+            tq, tk, tv = (filled((int(offs[-1]), w.heads, w.head_dim)) for _ in range(3))
+            for r in ids:
+                if checked(l, r) and w.prefill_lens[r]:
+                    for t_, kind in ((tq, synth.Q_PREFILL), (tk, synth.K_PREFILL), (tv, synth.V_PREFILL)):
+                        t_[offs[r]: offs[r + 1]] = to_torch(inputs.prefill(l, kind, r), w.dtype)
+        else:
+            q = np.concatenate([inputs.prefill(l, synth.Q_PREFILL, r) for r in ids])
+            k = np.concatenate([inputs.prefill(l, synth.K_PREFILL, r) for r in ids])
+            v = np.concatenate([inputs.prefill(l, synth.V_PREFILL, r) for r in ids])
+            tq, tk, tv = (to_torch(x, w.dtype) for x in (q, k, v))
         out = torch.empty_like(tq)
         cache.prefill(l, ids, w.prefill_lens, bases, tq, tk, tv, out)
         if l in check_layers:
@@ -130,10 +151,17 @@ def run_gpu(sc: Scenario, inputs: Inputs, record_state: bool = True):
     dev = {}
     for l in layers:
         for kind in range(3):
-            arr = np.zeros((n, tmax, w.heads, w.head_dim), dtype=np.float32)
-            for r in ids:
-                arr[r, : total[r]] = inputs.decode(l, kind, r, total[r])
-            dev[(l, kind)] = to_torch(arr, w.dtype)
+            if sc.device_fill:
+                t_ = filled((n, tmax, w.heads, w.head_dim))
+                for r in ids:
+                    if checked(l, r):
+                        t_[r, : total[r]] = to_torch(inputs.decode(l, kind, r, total[r]), w.dtype)
+                dev[(l, kind)] = t_
+            else:
+                arr = np.zeros((n, tmax, w.heads, w.head_dim), dtype=np.float32)
+                for r in ids:
+                    arr[r, : total[r]] = inputs.decode(l, kind, r, total[r])
+                dev[(l, kind)] = to_torch(arr, w.dtype)
 
     t_gen = [0] * n
     pre = max(starts)
@@ -208,6 +236,16 @@ def sampled_steps(n_steps: int, window: int, every: int = 1024) -> List[int]:
     s = {0, 1, window - 2, window - 1, window, window + 1, 2 * window, n_steps - 1}
     s |= set(range(0, n_steps, every))
     return sorted(x for x in s if 0 <= x < n_steps)
+
+
+def sampled_rows(p_len: int, seed: int, extra: int = 24) -> List[int]:
+    """Prefill rows to check at full size: both ends, every 64/128-row tile
+    boundary near the start, and seeded random rows."""
+    s = {0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, 255, 256, p_len - 129, p_len - 128,
+         p_len - 65, p_len - 64, p_len - 2, p_len - 1}
+    rng = np.random.default_rng([seed, p_len])
+    s |= set(int(x) for x in rng.integers(0, max(p_len, 1), extra))
+    return sorted(x for x in s if 0 <= x < p_len)
 
 
 def ulp_bf16(x: np.ndarray) -> np.ndarray:
