@@ -218,7 +218,7 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0):
     kv = 0
     steps_done = 0
     t_dec = 0.0
-    per_req_budget = budget_s * 0.75 / len(reqs)
+    per_req_budget = budget_s * 0.8 / len(reqs)
     for r in reqs:
         p = w.prefill_lens[r]
         pk = synth.draw(w.seed, w.wid, layer, synth.K_PREFILL, r, (p, w.heads, w.head_dim),
@@ -228,7 +228,8 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0):
         rc = O.RingCache(p, w.window, w.heads, w.head_dim, w.rope_base)
         rc.load_prefill(pk, pv)
         s0 = starts[r] + w.window   # steady state: ring full
-        nmax = 64
+        nmax = 4096
+        nmax = min(nmax, w.max_positions - p - s0)
         dq, dk, dv = (synth.draw(w.seed, w.wid, layer, kind, r, (s0 + nmax, w.heads, w.head_dim),
                                  w.input_std, w.dtype) for kind in (3, 4, 5))
         for s in range(s0):           # fill the ring (untimed)

@@ -264,8 +264,11 @@ DecodePlan HostState::plan_decode(int32_t n, const int32_t *ids) const {
   if (cfg_.decode_split_tokens > 0) {
     s = cfg_.decode_split_tokens;
   } else {
-    int64_t per_task = ceil_div(sum * cfg_.num_heads, kDefaultTargetTasks);
-    s = std::max<int64_t>(kSplitQuantum, ceil_div(per_task, kSplitQuantum) * kSplitQuantum);
+    auto round64 = [](int64_t x) { return std::max<int64_t>(kSplitQuantum, ceil_div(x, kSplitQuantum) * kSplitQuantum); };
+    const int64_t work = sum * cfg_.num_heads;
+    const int64_t fill = round64(ceil_div(work, kWaveSlots));
+    s = std::max(round64(ceil_div(work, kDefaultTargetTasks)),
+                 std::min<int64_t>(kPreferredSplit, fill));
     auto count = [&](int64_t sz) {
       int64_t k = 0;
       for (int b = 0; b < n; ++b) k += ceil_div(lmax[b], sz);

@@ -20,7 +20,16 @@ namespace rswa {
 
 constexpr int kAlign = 256;
 constexpr int kSplitQuantum = 64;      // split sizes are multiples of this
-constexpr int kDefaultTargetTasks = 4096;
+// Split-KV planning (measured on MI355X): aim for about two rounds of
+// decode wavefronts (3 resident per SIMD x 4 SIMDs x 256 CUs = 3072 per
+// round), but do not cut splits below 256 keys when the batch fills one
+// round at that size.
+#ifndef RSWA_TARGET_TASKS
+#define RSWA_TARGET_TASKS 6144
+#endif
+constexpr int kDefaultTargetTasks = RSWA_TARGET_TASKS;
+constexpr int kWaveSlots = 3072;
+constexpr int kPreferredSplit = 256;
 constexpr int kDefaultMaxPositions = 32768;
 constexpr int64_t kDefaultMaxPrefillTokens = 262144;
 constexpr int kPrefillTileMin = 64;    // smallest prefill query tile of any kernel

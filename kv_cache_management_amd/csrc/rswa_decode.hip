@@ -14,6 +14,16 @@
 #include "kernels.hpp"
 #include "rswa.h"
 
+// Tuning knobs (defaults are the measured best on MI355X): cache-policy bits
+// of the key/value loads (2 = non-temporal: the cache is streamed once per
+// step and re-reading it from L2 never pays), and loads per lane per chunk.
+#ifndef RSWA_DECODE_LOAD_AUX
+#define RSWA_DECODE_LOAD_AUX 2
+#endif
+#ifndef RSWA_DECODE_NI
+#define RSWA_DECODE_NI 8
+#endif
+
 namespace rswa {
 namespace {
 
@@ -81,7 +91,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int EPL = Vec16<T>::N;      // elements per 16-byte load
   constexpr int LPR = D / EPL;          // lanes per key row
   constexpr int TPI = 64 / LPR;         // key rows per load instruction
-  constexpr int NI = LPR < 8 ? LPR : 8; // load instructions per chunk
+  constexpr int NI = LPR < RSWA_DECODE_NI ? LPR : RSWA_DECODE_NI;  // loads per chunk
   constexpr int CH = NI * TPI;          // keys per chunk
   constexpr int DUP = LPR / NI;         // lanes holding each score
   constexpr int SH = Log2<DUP>::value;
@@ -168,9 +178,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   uint32_t tab_next = 0;
   if constexpr (PAGED) stash_rows(table_entry(c0));
 #pragma unroll
-  for (int i = 0; i < NI; ++i) kr[i] = buf_load16(rk, row_offset(c0, i));
+  for (int i = 0; i < NI; ++i) kr[i] = buf_load16<RSWA_DECODE_LOAD_AUX>(rk, row_offset(c0, i));
 #pragma unroll
-  for (int i = 0; i < NI; ++i) vr[i] = buf_load16(rv, row_offset(c0, i));
+  for (int i = 0; i < NI; ++i) vr[i] = buf_load16<RSWA_DECODE_LOAD_AUX>(rv, row_offset(c0, i));
   if (PAGED && c0 + CH < end) tab_next = table_entry(c0 + CH);
 
   for (;;) {
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     if (more) {
       if constexpr (PAGED) stash_rows(tab_next);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) kr[i] = buf_load16(rk, row_offset(c0 + CH, i));
+      for (int i = 0; i < NI; ++i) kr[i] = buf_load16<RSWA_DECODE_LOAD_AUX>(rk, row_offset(c0 + CH, i));
       if (PAGED && c0 + 2 * CH < end) tab_next = table_entry(c0 + 2 * CH);
     }
     __builtin_amdgcn_wave_barrier();
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
     if (!more) break;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = buf_load16(rv, row_offset(c0 + CH, i));
+    for (int i = 0; i < NI; ++i) vr[i] = buf_load16<RSWA_DECODE_LOAD_AUX>(rv, row_offset(c0 + CH, i));
     c0 += CH;
   }
 
@@ -236,32 +246,62 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
 // Cross-split combine: one wavefront per (batch entry, head).
 // M = max_s m_s; out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Lanes load the (max, sum) pairs of 64 splits at once; the partial vectors
+// are then read split by split with independent loads (D / 64 per lane).
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int J = D / 64;
   const int b = blockIdx.x / a.heads;
   const int h = blockIdx.x % a.heads;
   const int k0 = a.split_off[b];
   const int k1 = a.split_off[b + 1];
   const int lane = threadIdx.x;
   float mx = -INFINITY;
-  for (int k = k0; k < k1; ++k) mx = fmaxf(mx, a.part_ml[(int64_t)k * a.heads + h].x);
+  for (int k = k0 + lane; k < k1; k += 64) mx = fmaxf(mx, a.part_ml[(int64_t)k * a.heads + h].x);
+  mx = wave_max(mx);
   float den = 0.f;
-  float acc[D / 64];
+  float acc[J];
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) acc[j] = 0.f;
-  for (int k = k0; k < k1; ++k) {
-    const float2 m_l = a.part_ml[(int64_t)k * a.heads + h];
-    if (m_l.y == 0.f) continue;  // split past the cache end: no keys
-    const float w = __builtin_amdgcn_exp2f(m_l.x - mx);
-    den += w * m_l.y;
-    const float *po = a.part_o + ((int64_t)k * a.heads + h) * D;
+  for (int j = 0; j < J; ++j) acc[j] = 0.f;
+  for (int kb = k0; kb < k1; kb += 64) {
+    const int k = kb + lane;
+    float wgt = 0.f;
+    if (k < k1) {
+      const float2 m_l = a.part_ml[(int64_t)k * a.heads + h];
+      // splits past the cache end carry (-inf, 0) and get weight 0
+      wgt = m_l.y > 0.f ? __builtin_amdgcn_exp2f(m_l.x - mx) : 0.f;
+      den = fmaf(wgt, m_l.y, den);
+    }
+    const int nk = min(64, k1 - kb);
+    int i = 0;
+    for (; i + 4 <= nk; i += 4) {
+      float wv[4], pv[4][J];
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j) acc[j] = fmaf(w, po[lane + 64 * j], acc[j]);
+      for (int u = 0; u < 4; ++u) {
+        wv[u] = __shfl(wgt, i + u);
+        const float *po = a.part_o + ((int64_t)(kb + i + u) * a.heads + h) * D + lane;
+#pragma unroll
+        for (int j = 0; j < J; ++j) pv[u][j] = po[64 * j];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (wv[u] > 0.f) acc[j] = fmaf(wv[u], pv[u][j], acc[j]);
+    }
+    for (; i < nk; ++i) {
+      const float wv = __shfl(wgt, i);
+      const float *po = a.part_o + ((int64_t)(kb + i) * a.heads + h) * D + lane;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (wv > 0.f) acc[j] = fmaf(wv, po[64 * j], acc[j]);
+    }
   }
+  den = wave_sum(den);
   T *out = (T *)a.out + ((int64_t)b * a.heads + h) * D;
   const float inv = 1.f / den;
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) out[lane + 64 * j] = from_f<T>(acc[j] * inv);
+  for (int j = 0; j < J; ++j) out[lane + 64 * j] = from_f<T>(acc[j] * inv);
 }
 
 template <typename F>
