@@ -13,9 +13,13 @@
 //     layout each lane owns one query column, so row max / sum are in-lane
 //     plus one exchange with lane ^ 32.
 //   O^T (D x 32) += V^T (D x 64) . P^T (64 x 32): B = the probabilities,
-//     straight from the S^T registers (converted to bf16), A = V^T read from
-//     an LDS tile stored transposed.  The key order inside each 16-key MFMA
-//     step follows the S^T register layout; V^T is read in the same order.
+//     straight from the S^T registers (converted to bf16), A = V^T, read
+//     from the row-major V tile with the transposing LDS read
+//     (ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
+//     j mod 4 of the 64-bit rows addressed by lanes 4e + j/4, e = 0..3, so
+//     one read turns a 4-key x 16-dim block into 4 keys per lane).  The key
+//     order inside each 16-key MFMA step follows the S^T register layout.
+//   The output is rescaled only when some lane's running max grew.
 // Keys come from the pool (already rotated by the cache write); queries are
 // rotated on load at their absolute positions.  Probabilities are rounded to
 // bf16 for the P.V product; accumulation is fp32.
@@ -34,7 +38,16 @@ using namespace dev;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 4 x bf16 from the transposing LDS read.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16 *p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const void *)p);
+  return __builtin_bit_cast(bf16x4, v);
+}
 
 constexpr int kBM = 128;  // query rows per block
 constexpr int kBN = 64;   // keys per tile
@@ -42,15 +55,17 @@ constexpr int kBN = 64;   // keys per tile
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
-  constexpr int KP = D + 8;        // K tile row stride in LDS (elements)
-  constexpr int VP = kBN + 8;      // V^T tile row stride in LDS (elements)
+  // LDS row strides (elements), chosen for conflict-free reads: K rows are
+  // read 16 per 128-bit pass (stride = 4 dwords mod 64 banks); V rows are
+  // read 4 keys at a time by the transposing read (stride = 16 dwords mod 64).
+  constexpr int KP = D + 8;
+  constexpr int VP = D + 32;
   constexpr int DB = D / 32;       // 32-dim blocks of the output
   constexpr int CPR = D / 8;       // 16-byte chunks per key row
-  constexpr int KLD = kBN * CPR / 256;        // K chunks per thread per tile
-  constexpr int VLD = (kBN / 4) * CPR;        // V (4-key x 8-dim) items per tile
+  constexpr int KLD = kBN * CPR / 256;        // 16-byte chunks per thread per tile
   static_assert(KLD >= 1 && kBN * CPR % 256 == 0, "tile must split evenly");
   __shared__ __attribute__((aligned(16))) bf16 lk[kBN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 lv[D * VP];
+  __shared__ __attribute__((aligned(16))) bf16 lv[kBN * VP];
 
   const int item = blockIdx.x / a.heads;
   const int h = blockIdx.x % a.heads;
@@ -107,11 +122,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int kend = min(p_len, qt * kBM + kBM);
   const int ntile = (kend + kBN - 1) / kBN;
 
-  // ---- tile loads: global -> registers -> LDS -----------------------------
-  uint4 kreg[KLD];
-  uint4 vreg[4];
-  const int vkq = tid % (kBN / 4);   // key quad of this thread's V item
-  const int vch = tid / (kBN / 4);   // 8-dim chunk of this thread's V item
+  // ---- tile loads: global -> registers -> LDS (both row-major) -------------
+  uint4 kreg[KLD], vreg[KLD];
   auto row_of = [&](int j) -> int64_t {
     return table ? (int64_t)table[base + j] : base + j;
   };
@@ -120,15 +132,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     for (int it = 0; it < KLD; ++it) {
       const int idx = tid + 256 * it;
       const int j = k0 + idx / CPR;
-      kreg[it] = j < kend ? *(const uint4 *)(Kp + row_of(j) * row_stride + (idx % CPR) * 8)
-                          : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < VLD) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = k0 + 4 * vkq + r;
-        vreg[r] = j < kend ? *(const uint4 *)(Vp + row_of(j) * row_stride + vch * 8)
-                           : make_uint4(0, 0, 0, 0);
+      if (j < kend) {
+        const int64_t off = row_of(j) * row_stride + (idx % CPR) * 8;
+        kreg[it] = *(const uint4 *)(Kp + off);
+        vreg[it] = *(const uint4 *)(Vp + off);
+      } else {
+        kreg[it] = make_uint4(0, 0, 0, 0);
+        vreg[it] = make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -137,23 +147,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     for (int it = 0; it < KLD; ++it) {
       const int idx = tid + 256 * it;
       *(uint4 *)(lk + (idx / CPR) * KP + (idx % CPR) * 8) = kreg[it];
-    }
-    if (tid < VLD) {
-      // Transpose 4 keys x 8 dims: dim e of keys 4kq..4kq+3 -> one 8-byte row piece.
-      const uint32_t *v0 = (const uint32_t *)&vreg[0];
-      const uint32_t *v1 = (const uint32_t *)&vreg[1];
-      const uint32_t *v2 = (const uint32_t *)&vreg[2];
-      const uint32_t *v3 = (const uint32_t *)&vreg[3];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const uint32_t a0 = (v0[e >> 1] >> sh) & 0xffffu, a1 = (v1[e >> 1] >> sh) & 0xffffu;
-        const uint32_t a2 = (v2[e >> 1] >> sh) & 0xffffu, a3 = (v3[e >> 1] >> sh) & 0xffffu;
-        uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-        *(uint2 *)(lv + (vch * 8 + e) * VP + 4 * vkq) = pk;
-      }
+      *(uint4 *)(lv + (idx / CPR) * VP + (idx % CPR) * 8) = vreg[it];
     }
   };
+  // Transposing-read address of this lane: in its 16-lane group, lane
+  // 4e + q points at key (4g + e), dims (16 * (group & 1) + 4q) of a 32-dim
+  // block; per MFMA step only a constant offset is added.
+  const int tp = lane & 15;
+  const bf16 *vtr = lv + (4 * g + (tp >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (tp & 3);
 
   if (ntile > 0) load_tile(0);
   for (int kt = 0; kt < ntile; ++kt) {
@@ -193,38 +194,44 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx * qscale);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      m_run = m_new;
+    }
     float lsum = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][r], qscale, -m_new));
-        lsum += p;
-        pf[j][r >> 3][r & 7] = (bf16)p;
+      for (int hh = 0; hh < 2; ++hh) {
+        f32x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(s[j][8 * hh + e], qscale, -m_run));
+          lsum += pv[e];
+        }
+        pf[j][hh] = __builtin_convertvector(pv, bf16x8);
       }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < DB; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    l_run += lsum;
 
     // O^T += V^T . P^T
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      const bf16 *vrow = lv + (32 * d + (lane & 31)) * VP + 4 * g;
+    for (int d = 0; d < DB; ++d)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const bf16x4 lo = *(const bf16x4 *)(vrow + 32 * j + 16 * hh);
-          const bf16x4 hi = *(const bf16x4 *)(vrow + 32 * j + 16 * hh + 8);
+          const bf16 *p0 = vtr + (32 * j + 16 * hh) * VP + 32 * d;
+          const bf16x4 lo = lds_read_tr4(p0);
+          const bf16x4 hi = lds_read_tr4(p0 + 8 * VP);
           const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[j][hh], o[d], 0, 0, 0);
         }
-    }
   }
 
   if (qi >= p_len) return;
