@@ -19,7 +19,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -188,8 +187,9 @@ def traffic_from_profile(workload: str):
     path = os.path.join(PROFILE_DIR, f"decode_split_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
-    src = os.path.join(ROOT, "kv_cache_management_amd", "csrc", "rswa_kernels.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    from kv_cache_management_amd.profsummary import kernel_source_sha
+
+    sha = kernel_source_sha("decode_split")
     rec = None
     for line in open(path):
         if line.startswith("<!-- traffic "):

@@ -72,9 +72,9 @@ int resolve_config(const rswa_config &in, Config *out, std::string *err) {
   if (((int64_t)c.max_positions + c.window) * row_bytes > (int64_t)UINT32_MAX)
     return fail(err, RSWA_E_UNSUPPORTED, "(max_positions + window) * heads * head_dim * elem_bytes "
                                          "must be < 2^32");
-  if (c.has_table && c.num_slots * row_bytes > (int64_t)UINT32_MAX)
+  if (c.has_table && c.num_slots * row_bytes > (int64_t)UINT32_MAX - 64)
     return fail(err, RSWA_E_UNSUPPORTED, "with a slot table, one layer of a pool "
-                                         "(num_slots * heads * head_dim * elem_bytes) must be < 2^32 bytes");
+                                         "(num_slots * heads * head_dim * elem_bytes) must be < 2^32 - 64 bytes");
   if (c.has_table) {
     if (c.slot_table_len < 1 || c.slot_table_len > INT32_MAX)
       return fail(err, RSWA_E_ARG, "slot_table_len must be in [1, 2^31-1] with a slot table");

@@ -70,6 +70,7 @@ struct PrefillArgs {
   void *out;
   const float2 *rope;
   float qscale;
+  uint32_t layer_bytes;       // bytes of one layer of a pool (< 2^32 - 64 with a slot table)
   int32_t n, heads, layer, num_tiles, tile;
   int64_t total_tokens;
 };

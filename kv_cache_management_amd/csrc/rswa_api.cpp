@@ -3,6 +3,7 @@
 // ring, and kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -306,6 +307,8 @@ int rswa_prefill(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids
     a.out = out;
     a.rope = c->rope();
     a.qscale = c->qscale;
+    a.layer_bytes = (uint32_t)std::min<int64_t>(
+        cf.num_slots * cf.num_heads * cf.head_dim * cf.elem_bytes(), UINT32_MAX);
     a.n = n;
     a.heads = cf.num_heads;
     a.layer = layer;
@@ -401,8 +404,8 @@ int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out, voi
     a.part_ml = (float2 *)(c->ws + c->lay.part_ml);
     a.rope = c->rope();
     a.qscale = c->qscale;
-    a.layer_bytes = (uint32_t)(c->cfg.num_slots * c->cfg.num_heads * c->cfg.head_dim *
-                               c->cfg.elem_bytes());
+    a.layer_bytes = (uint32_t)std::min<int64_t>(
+        c->cfg.num_slots * c->cfg.num_heads * c->cfg.head_dim * c->cfg.elem_bytes(), UINT32_MAX);
     a.n = n;
     a.heads = c->cfg.num_heads;
     a.window = c->cfg.window;

@@ -5,7 +5,9 @@
 // section 2.1); the page's eager path computes it with a full-matrix softmax
 // (section 三).  Here it is a flash-attention forward: one block per (query
 // tile of 128 rows, head, request), 4 wavefronts of 32 query rows each, key
-// tiles of 64 streamed through LDS, online softmax in base 2.
+// tiles of 64 streamed through double-buffered LDS, online softmax in base 2.
+// The loop is software-pipelined one tile deep: while the softmax of tile k
+// runs on the VALU, the scores of tile k + 1 run on the matrix cores.
 //
 // Per wavefront and key tile:
 //   S^T (64 keys x 32 queries) = K (64 x D) . Q^T (D x 32): A = K rows from
@@ -19,7 +21,9 @@
 //     j mod 4 of the 64-bit rows addressed by lanes 4e + j/4, e = 0..3, so
 //     one read turns a 4-key x 16-dim block into 4 keys per lane).  The key
 //     order inside each 16-key MFMA step follows the S^T register layout.
-//   The output is rescaled only when some lane's running max grew.
+//   The running max is raised (and the output rescaled) only when a row's
+//   max grows by more than 8 in log2 units, so probabilities stay <= 2^8;
+//   the final division by the row sum, taken against the same max, is exact.
 // Keys come from the pool (already rotated by the cache write); queries are
 // rotated on load at their absolute positions.  Probabilities are rounded to
 // bf16 for the P.V product; accumulation is fp32.
@@ -52,8 +56,18 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16 *p) {
 constexpr int kBM = 128;  // query rows per block
 constexpr int kBN = 64;   // keys per tile
 
+#ifndef RSWA_PREFILL_MIN_BLOCKS
+#define RSWA_PREFILL_MIN_BLOCKS 2
+#endif
+// Issue priority of the matrix-core phases (0 = leave priorities alone).
+#ifndef RSWA_PREFILL_PRIO
+#define RSWA_PREFILL_PRIO 0
+#endif
+#define RSWA_PRIO_UP() do { if (RSWA_PREFILL_PRIO) __builtin_amdgcn_s_setprio(RSWA_PREFILL_PRIO); } while (0)
+#define RSWA_PRIO_DOWN() do { if (RSWA_PREFILL_PRIO) __builtin_amdgcn_s_setprio(0); } while (0)
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   // LDS row strides (elements), chosen for conflict-free reads: K rows are
   // read 16 per 128-bit pass (stride = 4 dwords mod 64 banks); V rows are
@@ -64,8 +78,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int CPR = D / 8;       // 16-byte chunks per key row
   constexpr int KLD = kBN * CPR / 256;        // 16-byte chunks per thread per tile
   static_assert(KLD >= 1 && kBN * CPR % 256 == 0, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) bf16 lk[kBN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 lv[kBN * VP];
+  __shared__ __attribute__((aligned(16))) bf16 lk[2][kBN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 lv[2][kBN * VP];
 
   const int item = blockIdx.x / a.heads;
   const int h = blockIdx.x % a.heads;
@@ -76,13 +90,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int64_t cu = a.cu[b];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 5;
   const int q0 = qt * kBM + w * 32;   // first query row of this wave
   const int qi = q0 + (lane & 31);    // query row of this lane
   const int row_stride = a.heads * D;
-  const bf16 *Kp = (const bf16 *)a.pool.k + (int64_t)a.layer * a.pool.layer_stride + h * D;
-  const bf16 *Vp = (const bf16 *)a.pool.v + (int64_t)a.layer * a.pool.layer_stride + h * D;
   const int32_t *table = a.pool.table;
 
   // ---- queries: B operand fragments, rotated at their positions ----------
@@ -123,62 +135,65 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int ntile = (kend + kBN - 1) / kBN;
 
   // ---- tile loads: global -> registers -> LDS (both row-major) -------------
+  // 32-bit buffer offsets: contiguous rows use a resource over this request's
+  // first kend rows (keys past kend read zero); paged rows use a resource over
+  // the layer and an offset past its end for keys past kend.
   uint4 kreg[KLD], vreg[KLD];
-  auto row_of = [&](int j) -> int64_t {
-    return table ? (int64_t)table[base + j] : base + j;
-  };
+  const uint32_t row_bytes = (uint32_t)row_stride * 2u;
+  const size_t layer_off = (size_t)a.layer * a.pool.layer_stride * 2;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  if (table) {
+    rk = make_rsrc((const char *)a.pool.k + layer_off, a.layer_bytes);
+    rv = make_rsrc((const char *)a.pool.v + layer_off, a.layer_bytes);
+  } else {
+    const size_t req_off = layer_off + (size_t)base * row_bytes;
+    rk = make_rsrc((const char *)a.pool.k + req_off, (uint32_t)kend * row_bytes);
+    rv = make_rsrc((const char *)a.pool.v + req_off, (uint32_t)kend * row_bytes);
+  }
+  const uint32_t col_off = (uint32_t)(h * D * 2 + (tid % CPR) * 16);
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < KLD; ++it) {
-      const int idx = tid + 256 * it;
-      const int j = k0 + idx / CPR;
-      if (j < kend) {
-        const int64_t off = row_of(j) * row_stride + (idx % CPR) * 8;
-        kreg[it] = *(const uint4 *)(Kp + off);
-        vreg[it] = *(const uint4 *)(Vp + off);
-      } else {
-        kreg[it] = make_uint4(0, 0, 0, 0);
-        vreg[it] = make_uint4(0, 0, 0, 0);
-      }
+      const int j = k0 + (tid + 256 * it) / CPR;
+      uint32_t off;
+      if (table)
+        off = j < kend ? (uint32_t)table[base + j] * row_bytes + col_off : a.layer_bytes;
+      else
+        off = (uint32_t)j * row_bytes + col_off;
+      kreg[it] = buf_load16(rk, off);
+      vreg[it] = buf_load16(rv, off);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < KLD; ++it) {
       const int idx = tid + 256 * it;
-      *(uint4 *)(lk + (idx / CPR) * KP + (idx % CPR) * 8) = kreg[it];
-      *(uint4 *)(lv + (idx / CPR) * VP + (idx % CPR) * 8) = vreg[it];
+      *(uint4 *)(lk[buf] + (idx / CPR) * KP + (idx % CPR) * 8) = kreg[it];
+      *(uint4 *)(lv[buf] + (idx / CPR) * VP + (idx % CPR) * 8) = vreg[it];
     }
   };
   // Transposing-read address of this lane: in its 16-lane group, lane
   // 4e + q points at key (4g + e), dims (16 * (group & 1) + 4q) of a 32-dim
   // block; per MFMA step only a constant offset is added.
   const int tp = lane & 15;
-  const bf16 *vtr = lv + (4 * g + (tp >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (tp & 3);
+  const int vtr = (4 * g + (tp >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (tp & 3);
 
-  if (ntile > 0) load_tile(0);
-  for (int kt = 0; kt < ntile; ++kt) {
-    const int k0 = kt * kBN;
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < ntile) load_tile(k0 + kBN);
-    if (k0 > q0 + 31) continue;  // tile entirely above this wave's diagonal
-
-    // S^T = K . Q^T, two 32-key blocks
-    f32x16 s[2];
+  // S^T = K . Q^T for the tile in LDS buffer `buf`, two 32-key blocks.
+  auto scores = [&](int buf, f32x16 *s) {
+    RSWA_PRIO_UP();
+    const f32x16 zero = {};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[j][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = *(const bf16x8 *)(lk + (32 * j + (lane & 31)) * KP + 16 * ks + 8 * g);
-        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[j], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 ka = *(const bf16x8 *)(lk[buf] + (32 * j + (lane & 31)) * KP + 16 * ks + 8 * g);
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? zero : s[j], 0, 0, 0);
       }
-    }
-    // causal mask (key > query) on tiles that reach the diagonal
-    if (k0 + kBN - 1 > q0) {
+    RSWA_PRIO_DOWN();
+  };
+  // Online softmax of tile k0's scores and O^T += V^T . P^T from buffer `buf`.
+  auto softmax_pv = [&](f32x16 *s, int buf, int k0) {
+    if (k0 + kBN - 1 > q0) {  // causal mask on tiles that reach the diagonal
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -193,8 +208,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * qscale);
-    if (__any(m_new > m_run)) {
+    const float m_cand = mx * qscale;
+    const bool grow = m_cand > m_run + 8.f;
+    if (__any(grow)) {
+      const float m_new = grow ? m_cand : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -218,20 +235,49 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         pf[j][hh] = __builtin_convertvector(pv, bf16x8);
       }
     l_run += lsum;
+    // V^T operands read one MFMA step ahead of their use.
+    RSWA_PRIO_UP();
+    auto v_operand = [&](int step) -> bf16x8 {
+      const int d = step / 4, j = (step / 2) % 2, hh = step % 2;
+      const bf16 *p0 = lv[buf] + vtr + (32 * j + 16 * hh) * VP + 32 * d;
+      const bf16x4 lo = lds_read_tr4(p0);
+      const bf16x4 hi = lds_read_tr4(p0 + 8 * VP);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 va = v_operand(0);
+#pragma unroll
+    for (int step = 0; step < 4 * DB; ++step) {
+      const bf16x8 vnext = step + 1 < 4 * DB ? v_operand(step + 1) : va;
+      const int d = step / 4, j = (step / 2) % 2, hh = step % 2;
+      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[j][hh], o[d], 0, 0, 0);
+      va = vnext;
+    }
+    RSWA_PRIO_DOWN();
+  };
 
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int d = 0; d < DB; ++d)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16 *p0 = vtr + (32 * j + 16 * hh) * VP + 32 * d;
-          const bf16x4 lo = lds_read_tr4(p0);
-          const bf16x4 hi = lds_read_tr4(p0 + 8 * VP);
-          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[j][hh], o[d], 0, 0, 0);
-        }
+  // Tile k lives in LDS buffer k & 1; tile k + 1 is staged from registers at
+  // the top of iteration k and tile k + 2 is fetched into registers meanwhile.
+  // A wave takes part in tile k only if k * kBN <= its last query row.
+  const int last_q = q0 + 31;
+  f32x16 s_cur[2], s_nxt[2];
+  load_tile(0);
+  store_tile(0);
+  if (ntile > 1) load_tile(kBN);
+  __syncthreads();
+  scores(0, s_cur);
+  for (int kt = 0; kt < ntile; ++kt) {
+    const int cur = kt & 1;
+    __syncthreads();  // every wave is done with tile kt - 1 (buffer cur ^ 1)
+    if (kt + 1 < ntile) store_tile(cur ^ 1);
+    __syncthreads();
+    if (kt + 2 < ntile) load_tile((kt + 2) * kBN);
+    const bool next = kt + 1 < ntile && (kt + 1) * kBN <= last_q;
+    if (next) scores(cur ^ 1, s_nxt);
+    if (kt * kBN <= last_q) softmax_pv(s_cur, cur, kt * kBN);
+    if (next) {
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
+    }
   }
 
   if (qi >= p_len) return;

@@ -9,7 +9,7 @@
 `trace` reads a `--kernel-trace --stats --output-format csv` directory and
 reports rocprofv3's own per-kernel statistics plus the mean duration of the
 last N dispatches of one kernel (the measured steps of a benchmark run come
-last).  `pmc` reads `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of the
+last, or use --measured-grid).  `pmc` reads `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of the
 benchmark and of a plain 1 GiB device copy, scales each counter by what it
 reads for the copy of known size, and reports HBM bytes per dispatch.
 """
@@ -42,7 +42,7 @@ def kernel_source_sha(kernel: str) -> str:
     return hashlib.sha256(data).hexdigest()[:16]
 
 
-def trace_summary(d: str, kernel: str, last: int, command: str) -> str:
+def trace_summary(d: str, kernel: str, last: int, command: str, max_grid: bool = False) -> str:
     stats = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
     trace = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv")))))
     lines = [f"# rocprofv3 kernel trace: {kernel} ({os.path.basename(d.rstrip('/'))})", "",
@@ -57,9 +57,22 @@ def trace_summary(d: str, kernel: str, last: int, command: str) -> str:
                      f"{float(r['Percentage']):.2f} |")
     sel = [r for r in trace if kernel in r.get("Kernel_Name", "")]
     sel.sort(key=lambda r: int(r["Start_Timestamp"]))
+    what = "all dispatches"
+    if max_grid:
+        # The measured decode steps all run the full batch with one plan, so
+        # their grid is the most frequent one.
+        gsz = lambda r: int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        counts = {}
+        for r in sel:
+            counts[gsz(r)] = counts.get(gsz(r), 0) + 1
+        gmode = max(counts, key=counts.get)
+        sel = [r for r in sel if gsz(r) == gmode]
+        what = f"dispatches with the full-batch grid ({gmode} work-items)"
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel]
     tail = durs[-last:] if last else durs
-    lines += ["", f"`{kernel}`: {len(durs)} dispatches; the last {len(tail)} (the measured steps): "
+    if last:
+        what += f", last {len(tail)}"
+    lines += ["", f"`{kernel}`, {what}: {len(tail)} dispatches, "
               f"mean {statistics.mean(tail):.2f} us, median {statistics.median(tail):.2f} us, "
               f"min {min(tail):.2f} us, max {max(tail):.2f} us.", ""]
     return "\n".join(lines)
@@ -120,6 +133,9 @@ def main(argv=None):
     t.add_argument("--kernel", required=True)
     t.add_argument("--last", type=int, default=0)
     t.add_argument("--command", required=True)
+    t.add_argument("--measured-grid", dest="max_grid", action="store_true",
+                   help="only dispatches with the kernel's most frequent grid (the "
+                        "full-batch measured steps)")
     t.add_argument("--out")
     p = sub.add_parser("pmc")
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
@@ -131,7 +147,7 @@ def main(argv=None):
     p.add_argument("--out")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        text = trace_summary(a.dir, a.kernel, a.last, a.command)
+        text = trace_summary(a.dir, a.kernel, a.last, a.command, a.max_grid)
     else:
         text = pmc_summary(a.fetch, a.write, a.copy_fetch, a.copy_write, a.kernel, a.last,
                            a.algorithmic_bytes, a.command)
