@@ -108,7 +108,7 @@ PrefillBlob PrefillBlob::make(int n, int64_t t) {
 }
 
 size_t PrefillBlob::capacity(const Config &c) {
-  return make(c.max_requests, c.max_prefill_tiles()).bytes;
+  return make(c.max_requests, c.max_prefill_blocks()).bytes;
 }
 
 Layout make_layout(const Config &c) {
@@ -211,18 +211,70 @@ PrefillPlan HostState::plan_prefill(int32_t n, const int32_t *plen, int32_t tile
     p.max_len = std::max(p.max_len, plen[b]);
   }
   p.total_tokens = p.cu[n];
-  struct Item { int32_t b, qt; };
-  std::vector<Item> items;
-  for (int b = 0; b < n; ++b)
-    for (int32_t qt = 0; qt < ceil_div(plen[b], tile); ++qt) items.push_back({b, qt});
-  // Longest rows first: a causal query tile qt covers (qt + 1) * tile keys.
-  std::stable_sort(items.begin(), items.end(),
-                   [](const Item &a, const Item &b) { return a.qt > b.qt; });
-  p.tiles.reserve(items.size() * 2);
-  for (const Item &it : items) {
-    p.tiles.push_back(it.b);
-    p.tiles.push_back(it.qt);
+  const int heads = cfg_.num_heads;
+  struct Item { int32_t b, qt, h; };
+  struct Group { int32_t b, h, tiles; int64_t work; };
+  std::vector<Group> groups;
+  int64_t n_items = 0;
+  for (int b = 0; b < n; ++b) {
+    const int32_t nt = (int32_t)ceil_div(plen[b], tile);
+    if (nt == 0) continue;
+    for (int h = 0; h < heads; ++h) groups.push_back({b, h, nt, (int64_t)nt * (nt + 1) / 2});
+    n_items += (int64_t)nt * heads;
   }
+  // Longest-processing-time assignment to XCDs, by whole (request, head)
+  // group when there are enough groups, else by single block.
+  std::vector<std::vector<Item>> xcd(kNumXcds);
+  std::vector<int64_t> load(kNumXcds, 0);
+  auto least = [&]() {
+    return (int)(std::min_element(load.begin(), load.end()) - load.begin());
+  };
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const Group &x, const Group &y) { return x.work > y.work; });
+  bool affinity = groups.size() >= (size_t)kXcdAffinityGroups;
+  if (affinity) {
+    for (const Group &g : groups) {
+      const int x = least();
+      for (int32_t qt = g.tiles - 1; qt >= 0; --qt) xcd[x].push_back({g.b, qt, g.h});
+      load[x] += g.work;
+    }
+    size_t longest = 0;
+    for (auto &l : xcd) longest = std::max(longest, l.size());
+    if ((int64_t)longest * kNumXcds > 2 * n_items + 64) {  // too much padding
+      affinity = false;
+      for (auto &l : xcd) l.clear();
+      std::fill(load.begin(), load.end(), 0);
+    }
+  }
+  if (!affinity) {
+    std::vector<Item> items;
+    items.reserve(n_items);
+    for (const Group &g : groups)
+      for (int32_t qt = 0; qt < g.tiles; ++qt) items.push_back({g.b, qt, g.h});
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item &x, const Item &y) { return x.qt > y.qt; });
+    for (const Item &it : items) {
+      const int x = least();
+      xcd[x].push_back(it);
+      load[x] += it.qt + 1;
+    }
+  }
+  size_t longest = 0;
+  for (auto &l : xcd) longest = std::max(longest, l.size());
+  p.tiles.reserve(2 * longest * kNumXcds);
+  for (size_t k = 0; k < longest; ++k)
+    for (int x = 0; x < kNumXcds; ++x) {
+      if (k < xcd[x].size()) {
+        const Item &it = xcd[x][k];
+        p.tiles.push_back(it.b);
+        p.tiles.push_back((it.qt << 16) | it.h);
+      } else {
+        p.tiles.push_back(-1);
+        p.tiles.push_back(0);
+      }
+    }
+  // Trailing empty slots need no launch.
+  while (p.tiles.size() >= 2 && p.tiles[p.tiles.size() - 2] < 0) p.tiles.resize(p.tiles.size() - 2);
   return p;
 }
 

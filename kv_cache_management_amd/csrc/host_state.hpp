@@ -49,6 +49,9 @@ struct Config {
   int64_t max_prefill_tiles() const {
     return max_prefill_tokens / kPrefillTileMin + max_requests;
   }
+  // Launch slots of one prefill call: every (query tile, head) block plus
+  // the padding the XCD interleave may add.
+  int64_t max_prefill_blocks() const { return 2 * max_prefill_tiles() * num_heads + 64; }
 };
 
 // Byte offsets of each workspace region (all 256-byte aligned).
@@ -86,7 +89,7 @@ struct PrefillBlob {  // for n requests and t query tiles
   size_t plen = 0;       // int32 [n]
   size_t cu = 0;         // int64 [n + 1]  packed token offset of request b
   size_t base = 0;       // int64 [n]
-  size_t tiles = 0;      // int32 [2t]     (b, query tile index)
+  size_t tiles = 0;      // int32 [2t]     launch slots: (b, qt << 16 | head), b < 0 = empty
   size_t bytes = 0;
   static PrefillBlob make(int n, int64_t t);
   static size_t capacity(const Config &c);
@@ -106,12 +109,20 @@ struct DecodePlan {
   int32_t num_splits() const { return (int32_t)split_map.size() / 2; }
 };
 
+constexpr int kNumXcds = 8;            // MI355X: workgroup i runs on XCD i mod 8
+constexpr int kXcdAffinityGroups = 32; // (request, head) groups needed for affinity
+
 struct PrefillPlan {
   int32_t tile = 0;
   int64_t total_tokens = 0;
   int32_t max_len = 0;
   std::vector<int64_t> cu;         // n + 1
-  std::vector<int32_t> tiles;      // 2 * num_tiles, longest rows first
+  // Launch order of (query tile, head) blocks: slot i holds
+  // (b, qt << 16 | head), or b = -1 for an empty slot.  Slot i runs on XCD
+  // i mod 8; each XCD's slots hold whole (request, head) groups (when there
+  // are enough of them) with the longest query tiles first, so blocks that
+  // share keys and values run on the same L2.
+  std::vector<int32_t> tiles;
   int64_t num_tiles() const { return (int64_t)tiles.size() / 2; }
 };
 
@@ -129,6 +140,7 @@ class HostState {
   // Plans the packed offsets and the query tiles (of `tile` rows) of a
   // checked prefill call.
   PrefillPlan plan_prefill(int32_t n, const int32_t *plen, int32_t tile) const;
+  // Work of a causal query tile: number of key tiles it covers.
 
   int check_set_batch(int32_t n, const int32_t *ids, std::string *err) const;
   DecodePlan plan_decode(int32_t n, const int32_t *ids) const;

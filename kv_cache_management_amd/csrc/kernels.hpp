@@ -63,7 +63,7 @@ struct PrefillArgs {
   const int32_t *plen;        // [n]
   const int64_t *cu;          // [n + 1] packed token offsets
   const int64_t *base;        // [n]
-  const int32_t *tiles;       // [2 * num_tiles] (batch entry, query tile)
+  const int32_t *tiles;       // [2 * num_tiles] launch slots (b, qt << 16 | head); b < 0 empty
   const void *q;              // [total][H][D]
   const void *k;
   const void *v;

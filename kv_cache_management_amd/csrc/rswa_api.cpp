@@ -277,8 +277,8 @@ int rswa_prefill(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids
     rswa::PrefillPlan plan = c->st.plan_prefill(n, prefill_len, tile);
     if (plan.total_tokens > 0 && (!q || !k || !v || !out))
       return c->fail(RSWA_E_ARG, "null q/k/v/out with prefill tokens");
-    if (plan.num_tiles() > cf.max_prefill_tiles())
-      return c->fail(RSWA_E_CAPACITY, "too many prefill tiles");
+    if (plan.num_tiles() > cf.max_prefill_blocks())
+      return c->fail(RSWA_E_CAPACITY, "too many prefill blocks");
     hipStream_t s = (hipStream_t)stream;
 
     rswa::PrefillBlob pb = rswa::PrefillBlob::make(n, plan.num_tiles());

@@ -124,10 +124,10 @@ __global__ __launch_bounds__(64) void prefill_attn_valu_kernel(PrefillArgs a) {
   constexpr int KT = 32;
   __shared__ float ks[KT][D];
   __shared__ float vs[KT][D];
-  const int item = blockIdx.x / a.heads;
-  const int h = blockIdx.x % a.heads;
-  const int b = a.tiles[2 * item];
-  const int qt = a.tiles[2 * item + 1];
+  const int b = a.tiles[2 * blockIdx.x];
+  if (b < 0) return;  // empty launch slot
+  const int qt = a.tiles[2 * blockIdx.x + 1] >> 16;
+  const int h = a.tiles[2 * blockIdx.x + 1] & 0xffff;
   const int p_len = a.plen[b];
   const int64_t base = a.base[b];
   const int64_t cu = a.cu[b];
@@ -238,7 +238,7 @@ hipError_t launch_prefill_attention(const PrefillArgs &a, int dtype, int head_di
   return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
     using T = decltype(tv);
     constexpr int D = decltype(dv)::value;
-    hipLaunchKernelGGL((prefill_attn_valu_kernel<T, D>), dim3(a.num_tiles * a.heads), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn_valu_kernel<T, D>), dim3(a.num_tiles), dim3(64), 0, s, a);
     return hipGetLastError();
   });
 }

@@ -81,10 +81,10 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
   __shared__ __attribute__((aligned(16))) bf16 lk[2][kBN * KP];
   __shared__ __attribute__((aligned(16))) bf16 lv[2][kBN * VP];
 
-  const int item = blockIdx.x / a.heads;
-  const int h = blockIdx.x % a.heads;
-  const int b = a.tiles[2 * item];
-  const int qt = a.tiles[2 * item + 1];
+  const int b = a.tiles[2 * blockIdx.x];
+  if (b < 0) return;  // empty launch slot
+  const int qt = a.tiles[2 * blockIdx.x + 1] >> 16;
+  const int h = a.tiles[2 * blockIdx.x + 1] & 0xffff;
   const int p_len = a.plen[b];
   const int64_t base = a.base[b];
   const int64_t cu = a.cu[b];
@@ -303,7 +303,7 @@ bool prefill_mfma_supported(int dtype, int head_dim) {
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, int head_dim, hipStream_t s) {
   if (a.num_tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.num_tiles * a.heads));
+  const dim3 grid((unsigned)a.num_tiles);
   if (head_dim == 128)
     hipLaunchKernelGGL((prefill_mfma_kernel<128>), grid, dim3(256), 0, s, a);
   else if (head_dim == 64)

@@ -4,6 +4,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <deque>
+#include <map>
+#include <tuple>
 #include <set>
 #include <string>
 #include <vector>
@@ -135,11 +137,59 @@ static void test_prefill_order_and_errors() {
   st.commit_prefill(1, 2, ids, pl, base);
   CHECK(st.check_prefill(1, 2, ids, pl, base, &err) == RSWA_E_STATE);   // layer 1 again
   CHECK(st.check_set_batch(2, ids, &err) == RSWA_OK);
-  // prefill plan: tiles cover each row once, longest first
+  // prefill plan: every (query tile, head) block once, empty slots marked
   PrefillPlan pp = st.plan_prefill(2, pl, 64);
   CHECK(pp.total_tokens == 100 && pp.cu[1] == 100 && pp.cu[2] == 100);
-  CHECK(pp.num_tiles() == 2);
-  CHECK(pp.tiles[0] == 0 && pp.tiles[1] == 1 && pp.tiles[2] == 0 && pp.tiles[3] == 0);
+  std::set<std::tuple<int, int, int>> seen;
+  for (int64_t i = 0; i < pp.num_tiles(); ++i) {
+    const int b = pp.tiles[2 * i];
+    if (b < 0) continue;
+    CHECK(seen.insert({b, pp.tiles[2 * i + 1] >> 16, pp.tiles[2 * i + 1] & 0xffff}).second);
+  }
+  CHECK(seen.size() == 2 * 10);  // request 0: 2 tiles x 10 heads; request 3 is empty
+  CHECK(pp.num_tiles() <= 24);
+}
+
+// With many (request, head) groups every group stays on one XCD (slot i runs
+// on XCD i mod 8), its query tiles longest first, and XCD work is balanced.
+static void test_prefill_xcd_plan() {
+  rswa_config rc = base_cfg();
+  rc.max_requests = 64;
+  rc.max_positions = 32768;
+  rc.num_slots = 64 * 9000;
+  rc.max_prefill_tokens = 1 << 20;
+  Config c = resolved(rc);
+  HostState st(c);
+  std::vector<int32_t> pl(64);
+  for (int i = 0; i < 64; ++i) pl[i] = 272 + (i * 7919) % 8000;
+  PrefillPlan pp = st.plan_prefill(64, pl.data(), 128);
+  std::map<std::pair<int, int>, std::vector<std::pair<int64_t, int>>> where;
+  std::vector<int64_t> work(8, 0);
+  int64_t items = 0;
+  for (int64_t i = 0; i < pp.num_tiles(); ++i) {
+    const int b = pp.tiles[2 * i];
+    if (b < 0) continue;
+    const int qt = pp.tiles[2 * i + 1] >> 16, h = pp.tiles[2 * i + 1] & 0xffff;
+    where[{b, h}].push_back({i, qt});
+    work[i % 8] += qt + 1;
+    ++items;
+  }
+  int64_t expect = 0;
+  for (int i = 0; i < 64; ++i) expect += 10 * ((pl[i] + 127) / 128);
+  CHECK(items == expect);
+  CHECK((int64_t)where.size() == 640);
+  for (auto &kv : where) {
+    const auto &v = kv.second;
+    CHECK((int)v.size() == (pl[kv.first.first] + 127) / 128);
+    for (size_t k = 0; k < v.size(); ++k) {
+      CHECK(v[k].first % 8 == v[0].first % 8);      // one XCD
+      CHECK(v[k].second == (int)(v.size() - 1 - k));  // longest first
+    }
+  }
+  const int64_t mx = *std::max_element(work.begin(), work.end());
+  const int64_t mn = *std::min_element(work.begin(), work.end());
+  CHECK(mx - mn <= mx / 50);  // within 2 %
+  CHECK(pp.num_tiles() <= c.max_prefill_blocks());
 }
 
 static void register_all(HostState &st, int n, const int32_t *ids, const int32_t *pl,
@@ -252,6 +302,7 @@ int main() {
   test_config();
   test_layout();
   test_prefill_order_and_errors();
+  test_prefill_xcd_plan();
   test_step_machine_and_ring();
   test_decode_plan();
   if (g_fail) {
