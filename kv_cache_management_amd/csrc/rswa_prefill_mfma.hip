@@ -66,7 +66,7 @@ constexpr int kBN = 64;   // keys per tile
 #define RSWA_PRIO_UP() do { if (RSWA_PREFILL_PRIO) __builtin_amdgcn_s_setprio(RSWA_PREFILL_PRIO); } while (0)
 #define RSWA_PRIO_DOWN() do { if (RSWA_PREFILL_PRIO) __builtin_amdgcn_s_setprio(0); } while (0)
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   // LDS row strides (elements), chosen for conflict-free reads: K rows are
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
   const uint32_t row_bytes = (uint32_t)row_stride * 2u;
   const size_t layer_off = (size_t)a.layer * a.pool.layer_stride * 2;
   __amdgpu_buffer_rsrc_t rk, rv;
-  if (table) {
+  if constexpr (PAGED) {
     rk = make_rsrc((const char *)a.pool.k + layer_off, a.layer_bytes);
     rv = make_rsrc((const char *)a.pool.v + layer_off, a.layer_bytes);
   } else {
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     for (int it = 0; it < KLD; ++it) {
       const int j = k0 + (tid + 256 * it) / CPR;
       uint32_t off;
-      if (table)
+      if constexpr (PAGED)
         off = j < kend ? (uint32_t)table[base + j] * row_bytes + col_off : a.layer_bytes;
       else
         off = (uint32_t)j * row_bytes + col_off;
@@ -192,8 +192,8 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     RSWA_PRIO_DOWN();
   };
   // Online softmax of tile k0's scores and O^T += V^T . P^T from buffer `buf`.
-  auto softmax_pv = [&](f32x16 *s, int buf, int k0) {
-    if (k0 + kBN - 1 > q0) {  // causal mask on tiles that reach the diagonal
+  auto softmax_pv = [&](f32x16 *s, int buf, int k0, bool may_mask) {
+    if (may_mask && k0 + kBN - 1 > q0) {  // causal mask on tiles that reach the diagonal
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -265,7 +265,24 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
   if (ntile > 1) load_tile(kBN);
   __syncthreads();
   scores(0, s_cur);
-  for (int kt = 0; kt < ntile; ++kt) {
+  // Steady state: tiles kt and kt + 1 lie wholly below the block's first
+  // query row (no mask, every wave takes part) and tile kt + 2 exists, so the
+  // body has no branch and the scores of kt + 1 can interleave with the
+  // softmax of kt.
+  const int steady = max(0, min(ntile - 2, 2 * qt - 1));
+  int kt = 0;
+  for (; kt < steady; ++kt) {
+    const int cur = kt & 1;
+    __syncthreads();
+    store_tile(cur ^ 1);
+    __syncthreads();
+    load_tile((kt + 2) * kBN);
+    scores(cur ^ 1, s_nxt);
+    softmax_pv(s_cur, cur, kt * kBN, false);
+    s_cur[0] = s_nxt[0];
+    s_cur[1] = s_nxt[1];
+  }
+  for (; kt < ntile; ++kt) {
     const int cur = kt & 1;
     __syncthreads();  // every wave is done with tile kt - 1 (buffer cur ^ 1)
     if (kt + 1 < ntile) store_tile(cur ^ 1);
@@ -273,7 +290,7 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     if (kt + 2 < ntile) load_tile((kt + 2) * kBN);
     const bool next = kt + 1 < ntile && (kt + 1) * kBN <= last_q;
     if (next) scores(cur ^ 1, s_nxt);
-    if (kt * kBN <= last_q) softmax_pv(s_cur, cur, kt * kBN);
+    if (kt * kBN <= last_q) softmax_pv(s_cur, cur, kt * kBN, true);
     if (next) {
       s_cur[0] = s_nxt[0];
       s_cur[1] = s_nxt[1];
@@ -304,10 +321,15 @@ bool prefill_mfma_supported(int dtype, int head_dim) {
 hipError_t launch_prefill_mfma(const PrefillArgs &a, int head_dim, hipStream_t s) {
   if (a.num_tiles == 0) return hipSuccess;
   const dim3 grid((unsigned)a.num_tiles);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((prefill_mfma_kernel<128>), grid, dim3(256), 0, s, a);
+  const bool paged = a.pool.table != nullptr;
+  if (head_dim == 128 && paged)
+    hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), grid, dim3(256), 0, s, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), grid, dim3(256), 0, s, a);
+  else if (head_dim == 64 && paged)
+    hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), grid, dim3(256), 0, s, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<64>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
