@@ -151,13 +151,25 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     rv = make_rsrc((const char *)a.pool.v + req_off, (uint32_t)kend * row_bytes);
   }
   const uint32_t col_off = (uint32_t)(h * D * 2 + (tid % CPR) * 16);
+  // Paged layout: slot-table entries of a tile are fetched one tile ahead of
+  // its key/value loads (rows_next), so the loads never wait on the table.
+  int32_t rows_next[KLD];
+  auto fetch_rows = [&](int k0) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int it = 0; it < KLD; ++it) {
+        const int j = k0 + (tid + 256 * it) / CPR;
+        rows_next[it] = j < kend ? table[base + j] : -1;
+      }
+    }
+  };
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < KLD; ++it) {
       const int j = k0 + (tid + 256 * it) / CPR;
       uint32_t off;
       if constexpr (PAGED)
-        off = j < kend ? (uint32_t)table[base + j] * row_bytes + col_off : a.layer_bytes;
+        off = rows_next[it] >= 0 ? (uint32_t)rows_next[it] * row_bytes + col_off : a.layer_bytes;
       else
         off = (uint32_t)j * row_bytes + col_off;
       kreg[it] = buf_load16(rk, off);
@@ -260,9 +272,12 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
   // A wave takes part in tile k only if k * kBN <= its last query row.
   const int last_q = q0 + 31;
   f32x16 s_cur[2], s_nxt[2];
+  fetch_rows(0);
   load_tile(0);
   store_tile(0);
+  fetch_rows(kBN);
   if (ntile > 1) load_tile(kBN);
+  fetch_rows(2 * kBN);
   __syncthreads();
   scores(0, s_cur);
   // Steady state: tiles kt and kt + 1 lie wholly below the block's first
@@ -277,6 +292,7 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     store_tile(cur ^ 1);
     __syncthreads();
     load_tile((kt + 2) * kBN);
+    fetch_rows((kt + 3) * kBN);
     scores(cur ^ 1, s_nxt);
     softmax_pv(s_cur, cur, kt * kBN, false);
     s_cur[0] = s_nxt[0];
@@ -287,7 +303,10 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     __syncthreads();  // every wave is done with tile kt - 1 (buffer cur ^ 1)
     if (kt + 1 < ntile) store_tile(cur ^ 1);
     __syncthreads();
-    if (kt + 2 < ntile) load_tile((kt + 2) * kBN);
+    if (kt + 2 < ntile) {
+      load_tile((kt + 2) * kBN);
+      fetch_rows((kt + 3) * kBN);
+    }
     const bool next = kt + 1 < ntile && (kt + 1) * kBN <= last_q;
     if (next) scores(cur ^ 1, s_nxt);
     if (kt * kBN <= last_q) softmax_pv(s_cur, cur, kt * kBN, true);
