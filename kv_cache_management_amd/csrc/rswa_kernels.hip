@@ -84,33 +84,45 @@ __device__ __forceinline__ int find_request(const int64_t *cu, int n, int64_t to
   return lo;
 }
 
-// One block per packed prefill token; threads cover (head, rotation pair).
+// Cache write of the prefill: TPP threads per (token, head); thread c moves
+// 16-byte pieces: elements [c*EPL, c*EPL + EPL) of the lower half and the
+// same offsets of the upper half (its rotation partners) of k and v.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_cache_write_kernel(PrefillArgs a) {
-  const int64_t tok = blockIdx.x;
+  constexpr int EPL = 16 / (int)sizeof(T);
+  constexpr int TPP = (D / 2) / EPL;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = gid / TPP;
+  if (pair >= a.total_tokens * a.heads) return;
+  const int c = (int)(gid % TPP);
+  const int64_t tok = pair / a.heads;
+  const int h = (int)(pair % a.heads);
   const int b = find_request(a.cu, a.n, tok);
   const int j = (int)(tok - a.cu[b]);
   const int64_t row = pool_row(a.pool.table, a.base[b], j);
-  const int64_t dst0 = (int64_t)a.layer * a.pool.layer_stride + row * a.heads * D;
-  const int64_t src0 = tok * a.heads * D;
-  const float2 *cs = a.rope + (int64_t)j * (D / 2);
-  for (int idx = threadIdx.x; idx < a.heads * (D / 2); idx += 256) {
-    const int h = idx / (D / 2);
-    const int i = idx % (D / 2);
-    const int64_t src = src0 + h * D;
-    const int64_t dst = dst0 + h * D;
-    const T *k = (const T *)a.k + src;
-    const T *v = (const T *)a.v + src;
-    T *K = (T *)a.pool.k + dst;
-    T *V = (T *)a.pool.v + dst;
-    const float2 c = cs[i];
-    const float x1 = to_f(k[i]);
-    const float x2 = to_f(k[i + D / 2]);
-    K[i] = from_f<T>(x1 * c.x - x2 * c.y);
-    K[i + D / 2] = from_f<T>(x2 * c.x + x1 * c.y);
-    V[i] = v[i];
-    V[i + D / 2] = v[i + D / 2];
+  const int64_t src = (tok * a.heads + h) * D + c * EPL;
+  const int64_t dst = (int64_t)a.layer * a.pool.layer_stride + (row * a.heads + h) * D + c * EPL;
+  const uint4 k1 = *(const uint4 *)((const T *)a.k + src);
+  const uint4 k2 = *(const uint4 *)((const T *)a.k + src + D / 2);
+  const uint4 v1 = *(const uint4 *)((const T *)a.v + src);
+  const uint4 v2 = *(const uint4 *)((const T *)a.v + src + D / 2);
+  float x1[EPL], x2[EPL];
+  Vec16<T>::unpack(k1, x1);
+  Vec16<T>::unpack(k2, x2);
+  const float2 *cs = a.rope + (int64_t)j * (D / 2) + c * EPL;
+  T r1[EPL], r2[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const float2 cc = cs[e];
+    r1[e] = from_f<T>(x1[e] * cc.x - x2[e] * cc.y);
+    r2[e] = from_f<T>(x2[e] * cc.x + x1[e] * cc.y);
   }
+  T *K = (T *)a.pool.k + dst;
+  T *V = (T *)a.pool.v + dst;
+  *(uint4 *)K = __builtin_bit_cast(uint4, *(const T(*)[EPL])r1);
+  *(uint4 *)(K + D / 2) = __builtin_bit_cast(uint4, *(const T(*)[EPL])r2);
+  *(uint4 *)V = v1;
+  *(uint4 *)(V + D / 2) = v2;
 }
 
 // ---------------------------------------------------------------------------
@@ -223,7 +235,10 @@ hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_
   return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
     using T = decltype(tv);
     constexpr int D = decltype(dv)::value;
-    hipLaunchKernelGGL((prefill_cache_write_kernel<T, D>), dim3((unsigned)a.total_tokens), dim3(256), 0, s, a);
+    constexpr int TPP = (D / 2) / (16 / (int)sizeof(T));
+    const int64_t threads = a.total_tokens * a.heads * TPP;
+    hipLaunchKernelGGL((prefill_cache_write_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
   });
 }
