@@ -57,7 +57,7 @@ def prefill_flops(w: W.Workload):
 class Job:
     """Device-resident inputs and the cache for one workload."""
 
-    def __init__(self, w: W.Workload, decode_steps: int, seed: int = 0):
+    def __init__(self, w: W.Workload, decode_steps: int, seed: int = 0, fused: bool = True):
         import torch
         from kv_cache_management_amd import rswa
 
@@ -66,6 +66,7 @@ class Job:
         self.lib = rswa.load()
         self.w = w
         self.steps = decode_steps
+        self.fused = fused
         dev = torch.device("cuda", torch.cuda.current_device())
         tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         n, H, D, L = w.batch, w.heads, w.head_dim, w.layers
@@ -133,6 +134,11 @@ class Job:
         for l in range(L):
             blk = self.dec_ptr0 + ((g * L + l) * 3) * self.row_bytes
             q, k, v = blk, blk + self.row_bytes, blk + 2 * self.row_bytes
+            if self.fused:
+                st = lib.rswa_decode_step_fused(h, l, q, k, v, self.out_ptr[l], s)
+                if st:
+                    self._check(st)
+                continue
             st = lib.rswa_ring_write(h, l, k, v, s)
             if st:
                 self._check(st)
@@ -274,6 +280,9 @@ def main():
     ap.add_argument("--workload", default="ragged_mix", choices=sorted(W.ALL))
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="measured decode steps per job (default: the workload's)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate rswa_ring_write + rswa_decode_step calls instead of "
+                         "rswa_decode_step_fused")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="do not time kernels with event pairs inside the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -307,7 +316,7 @@ def main():
     steps = args.decode_steps or w.decode_steps
     log(f"workload {w.name}: {w.batch} requests x {w.layers} layers, sum P = {sum(w.prefill_lens)}, "
         f"{steps} decode steps")
-    job = Job(w, steps)
+    job = Job(w, steps, fused=not args.unfused)
     torch.cuda.synchronize()
     for i in range(args.warmup):
         t0 = time.perf_counter()
@@ -369,7 +378,9 @@ def main():
         "config": {"workload": w.name, "requests": w.batch, "layers": w.layers, "heads": w.heads,
                    "head_dim": w.head_dim, "window": w.window, "decode_steps": steps,
                    "prefill_tokens": sum(w.prefill_lens),
-                   "kv_layout": "page-size-1 slot table" if w.paged else "contiguous"},
+                   "kv_layout": "page-size-1 slot table" if w.paged else "contiguous",
+                   "decode_call": "rswa_ring_write + rswa_decode_step" if args.unfused
+                   else "rswa_decode_step_fused"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_steps_per_s": round(steps * args.steps / dec_s, 2),
         "decode_ms_per_step": round(dec_s * 1e3 / (steps * args.steps), 4),

@@ -155,6 +155,16 @@ int rswa_ring_write(rswa_cache *c, int32_t layer, const void *k_new,
 int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out,
                      void *stream);
 
+/* rswa_ring_write followed by rswa_decode_step for `layer`, in fewer launches:
+ * the split-KV kernel itself performs the in-place slot write (the wave
+ * whose split holds slot P + (t mod W) writes the rotated key and the value
+ * for its head and attends with them).  Same inputs, results, state rules
+ * and errors as the two calls (RSWA_E_POSITION, RSWA_E_STATE if this layer
+ * was already written or decoded in this step); the pool holds the new row
+ * once this call's kernels have run. */
+int rswa_decode_step_fused(rswa_cache *c, int32_t layer, const void *q, const void *k_new,
+                           const void *v_new, void *out, void *stream);
+
 /* End the step: t += 1 for every active request.  Needs rswa_decode_step of
  * every layer in this step. */
 int rswa_advance(rswa_cache *c, void *stream);

@@ -58,6 +58,17 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// RoPE rotate-half of the pair (x1, x2) = (x_i, x_{i+D/2}) by the angle
+// whose (cos, sin) is cs: (x1 cos - x2 sin, x2 cos + x1 sin).  Each half is
+// one product plus one fused multiply-add, written out so that every kernel
+// that writes a key row rounds it identically.
+__device__ __forceinline__ float rope_lo(float x1, float x2, float2 cs) {
+  return fmaf(x1, cs.x, -(x2 * cs.y));
+}
+__device__ __forceinline__ float rope_hi(float x1, float x2, float2 cs) {
+  return fmaf(x2, cs.x, x1 * cs.y);
+}
+
 __device__ __forceinline__ int64_t pool_row(const int32_t *table, int64_t base, int64_t i) {
   return table ? (int64_t)table[base + i] : base + i;
 }

@@ -378,6 +378,15 @@ int HostState::check_decode(int32_t layer, std::string *err) const {
 
 void HostState::commit_decode(int32_t layer) { decoded_[layer] = 1; }
 
+int HostState::check_fused(int32_t layer, std::string *err) const {
+  return check_ring_write(layer, err);  // not written this step implies not decoded
+}
+
+void HostState::commit_fused(int32_t layer) {
+  written_[layer] = 1;
+  decoded_[layer] = 1;
+}
+
 int HostState::check_advance(std::string *err) const {
   if (batch_.empty()) return fail(err, RSWA_E_STATE, "no active batch (rswa_set_batch)");
   for (int l = 0; l < cfg_.num_layers; ++l)

@@ -150,6 +150,9 @@ class HostState {
   void commit_ring_write(int32_t layer);
   int check_decode(int32_t layer, std::string *err) const;
   void commit_decode(int32_t layer);
+  // Ring write and decode of one layer in one call.
+  int check_fused(int32_t layer, std::string *err) const;
+  void commit_fused(int32_t layer);
   int check_advance(std::string *err) const;
   void commit_advance();
 

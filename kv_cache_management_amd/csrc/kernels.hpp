@@ -48,6 +48,8 @@ struct DecodeArgs {
   const int32_t *split_off;   // [n + 1]
   const void *q;              // [n][H][D]
   void *out;                  // [n][H][D]
+  const void *k_new;          // [n][H][D] or null: ring write fused into the split kernel
+  const void *v_new;
   float *part_o;              // [num_splits][H][D]
   float2 *part_ml;            // [num_splits][H]  (running max in log2 units, sum)
   const float2 *rope;

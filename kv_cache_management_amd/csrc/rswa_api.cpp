@@ -380,48 +380,71 @@ int rswa_ring_write(rswa_cache *c, int32_t layer, const void *k_new, const void 
   });
 }
 
+}  // extern "C"
+
+namespace {
+
+int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, const void *v_new,
+                void *out, void *stream) {
+  const bool fused = k_new != nullptr || v_new != nullptr;
+  std::string err;
+  int rc = fused ? c->st.check_fused(layer, &err) : c->st.check_decode(layer, &err);
+  if (rc != RSWA_OK) return c->fail(rc, err);
+  if (!q || !out) return c->fail(RSWA_E_ARG, "null q / out");
+  if (fused && (!k_new || !v_new)) return c->fail(RSWA_E_ARG, "null k_new / v_new");
+  const rswa::DecodePlan &plan = c->st.plan();
+  const int n = (int)c->st.batch().size();
+  rswa::BatchBlob bb = rswa::BatchBlob::make(n, plan.num_splits());
+  const char *dev = c->ws + c->lay.batch;
+  rswa::DecodeArgs a{};
+  a.pool = c->pool();
+  a.pool.table = c->slot_table;
+  a.st = c->state();
+  a.batch_req = (const int32_t *)(dev + bb.req);
+  a.split_map = (const int32_t *)(dev + bb.split_map);
+  a.split_off = (const int32_t *)(dev + bb.split_off);
+  a.q = q;
+  a.out = out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.part_o = (float *)(c->ws + c->lay.part_o);
+  a.part_ml = (float2 *)(c->ws + c->lay.part_ml);
+  a.rope = c->rope();
+  a.qscale = c->qscale;
+  a.layer_bytes = (uint32_t)std::min<int64_t>(
+      c->cfg.num_slots * c->cfg.num_heads * c->cfg.head_dim * c->cfg.elem_bytes(), UINT32_MAX);
+  a.n = n;
+  a.heads = c->cfg.num_heads;
+  a.window = c->cfg.window;
+  a.layer = layer;
+  a.num_splits = plan.num_splits();
+  a.split_tokens = plan.split_tokens;
+  hipStream_t s = (hipStream_t)stream;
+  const int pi = c->prof_begin(RSWA_KERNEL_DECODE_SPLIT, s);
+  hipError_t e = rswa::launch_decode_split(a, c->cfg.dtype, c->cfg.head_dim, s);
+  c->prof_end(RSWA_KERNEL_DECODE_SPLIT, pi, s);
+  if (e != hipSuccess) return c->hip_fail(e, "split-KV decode launch");
+  e = rswa::launch_decode_combine(a, c->cfg.dtype, c->cfg.head_dim, s);
+  if (e != hipSuccess) return c->hip_fail(e, "decode combine launch");
+  if (fused) c->st.commit_fused(layer);
+  else c->st.commit_decode(layer);
+  return RSWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out, void *stream) {
   if (!c) return set_global_error(RSWA_E_ARG, "null handle");
-  return guarded(c, [&]() -> int {
-    std::string err;
-    int rc = c->st.check_decode(layer, &err);
-    if (rc != RSWA_OK) return c->fail(rc, err);
-    if (!q || !out) return c->fail(RSWA_E_ARG, "null q / out");
-    const rswa::DecodePlan &plan = c->st.plan();
-    const int n = (int)c->st.batch().size();
-    rswa::BatchBlob bb = rswa::BatchBlob::make(n, plan.num_splits());
-    const char *dev = c->ws + c->lay.batch;
-    rswa::DecodeArgs a{};
-    a.pool = c->pool();
-    a.pool.table = c->slot_table;
-    a.st = c->state();
-    a.batch_req = (const int32_t *)(dev + bb.req);
-    a.split_map = (const int32_t *)(dev + bb.split_map);
-    a.split_off = (const int32_t *)(dev + bb.split_off);
-    a.q = q;
-    a.out = out;
-    a.part_o = (float *)(c->ws + c->lay.part_o);
-    a.part_ml = (float2 *)(c->ws + c->lay.part_ml);
-    a.rope = c->rope();
-    a.qscale = c->qscale;
-    a.layer_bytes = (uint32_t)std::min<int64_t>(
-        c->cfg.num_slots * c->cfg.num_heads * c->cfg.head_dim * c->cfg.elem_bytes(), UINT32_MAX);
-    a.n = n;
-    a.heads = c->cfg.num_heads;
-    a.window = c->cfg.window;
-    a.layer = layer;
-    a.num_splits = plan.num_splits();
-    a.split_tokens = plan.split_tokens;
-    hipStream_t s = (hipStream_t)stream;
-    const int pi = c->prof_begin(RSWA_KERNEL_DECODE_SPLIT, s);
-    hipError_t e = rswa::launch_decode_split(a, c->cfg.dtype, c->cfg.head_dim, s);
-    c->prof_end(RSWA_KERNEL_DECODE_SPLIT, pi, s);
-    if (e != hipSuccess) return c->hip_fail(e, "split-KV decode launch");
-    e = rswa::launch_decode_combine(a, c->cfg.dtype, c->cfg.head_dim, s);
-    if (e != hipSuccess) return c->hip_fail(e, "decode combine launch");
-    c->st.commit_decode(layer);
-    return RSWA_OK;
-  });
+  return guarded(c, [&]() -> int { return decode_impl(c, layer, q, nullptr, nullptr, out, stream); });
+}
+
+int rswa_decode_step_fused(rswa_cache *c, int32_t layer, const void *q, const void *k_new,
+                           const void *v_new, void *out, void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  if (!k_new || !v_new) return c->fail(RSWA_E_ARG, "null k_new / v_new");
+  return guarded(c, [&]() -> int { return decode_impl(c, layer, q, k_new, v_new, out, stream); });
 }
 
 int rswa_advance(rswa_cache *c, void *stream) {

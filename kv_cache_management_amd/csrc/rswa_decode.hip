@@ -20,6 +20,9 @@
 #ifndef RSWA_DECODE_LOAD_AUX
 #define RSWA_DECODE_LOAD_AUX 2
 #endif
+#ifndef RSWA_DECODE_MIN_BLOCKS
+#define RSWA_DECODE_MIN_BLOCKS 1
+#endif
 #ifndef RSWA_DECODE_NI
 #define RSWA_DECODE_NI 8
 #endif
@@ -86,8 +89,8 @@ template <> struct Log2<1> { static constexpr int value = 0; };
 // reads zeros without touching memory.  Paged layout: the resource spans the
 // layer; tail keys reuse the last valid key's row and get probability 0.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool PAGED>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+template <typename T, int D, bool PAGED, bool FUSED>
+__global__ __launch_bounds__(256, RSWA_DECODE_MIN_BLOCKS) void decode_split_kernel(DecodeArgs a) {
   constexpr int EPL = Vec16<T>::N;      // elements per 16-byte load
   constexpr int LPR = D / EPL;          // lanes per key row
   constexpr int TPI = 64 / LPR;         // key rows per load instruction
@@ -98,9 +101,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   static_assert(CH <= 64, "chunk keys must fit one table load");
   __shared__ float lds_p[4][64];
   __shared__ int32_t lds_row[4][64];
+  __shared__ uint4 lds_new[FUSED ? 4 : 1][2][LPR];
 
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int task = blockIdx.x * 4 + wid;
   if (task >= a.num_splits * a.heads) return;
   const int ks = task / a.heads;
@@ -167,6 +171,59 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       return (uint32_t)(c0 + i * TPI + g) * row_bytes + lane_off;
   };
 
+  // Fused ring write: the wave whose split holds this step's ring slot
+  // rotates k_new at position P + t, stores the new key/value row for its
+  // head, and uses the new row in place of the stale one it loads.
+  const int slot_new = p_len + t % a.window;
+  const bool writes = FUSED && slot_new >= start && slot_new < end;
+  // This lane's 16-byte slices of the new rotated key row and value row.
+  auto new_row = [&](uint4 &kn_pk, uint4 &vn_pk) {
+    const T *kp = (const T *)a.k_new + ((int64_t)b * a.heads + h) * D;
+    const T *vp = (const T *)a.v_new + ((int64_t)b * a.heads + h) * D;
+    T kn[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int d = c * EPL + e;
+      const float2 cc = cs[d % (D / 2)];
+      if (d < D / 2) {
+        const float x1 = to_f(kp[d]), x2 = to_f(kp[d + D / 2]);
+        kn[e] = from_f<T>(rope_lo(x1, x2, cc));
+      } else {
+        const float x2 = to_f(kp[d]), x1 = to_f(kp[d - D / 2]);
+        kn[e] = from_f<T>(rope_hi(x1, x2, cc));
+      }
+    }
+    kn_pk = __builtin_bit_cast(uint4, kn);
+    vn_pk = *(const uint4 *)(vp + c * EPL);
+  };
+  // The new row goes to the pool and, for this wave's later use, to LDS.
+  if (writes) {
+    if (g == 0) {
+      uint4 kn_pk, vn_pk;
+      new_row(kn_pk, vn_pk);
+      lds_new[wid][0][c] = kn_pk;
+      lds_new[wid][1][c] = vn_pk;
+      const int64_t row = PAGED ? (int64_t)a.pool.table[base + slot_new] : base + slot_new;
+      const size_t off = layer_off + (size_t)row * row_bytes + lane_off;
+      *(uint4 *)((char *)a.pool.k + off) = kn_pk;
+      *(uint4 *)((char *)a.pool.v + off) = vn_pk;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // Replaces the stale loaded copy of the new slot (key c0 + i * TPI + g) in
+  // the chunk that holds it.
+  auto patch = [&](uint4 *regs, int c0, int which) {
+    if (writes && slot_new >= c0 && slot_new < c0 + CH) {
+      const int rel = slot_new - c0;
+      if (g == rel % TPI) {
+        const uint4 fresh = lds_new[wid][which][c];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          if (i == rel / TPI) regs[i] = fresh;
+      }
+    }
+  };
+
   float m_run = -INFINITY;
   float l_run = 0.f;
   float o[EPL];
@@ -185,6 +242,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   for (;;) {
     const bool more = c0 + CH < end;
+    patch(kr, c0, 0);
     float sc[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -213,6 +271,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       if (PAGED && c0 + 2 * CH < end) tab_next = table_entry(c0 + 2 * CH);
     }
     __builtin_amdgcn_wave_barrier();
+    patch(vr, c0, 1);
     // Key i * TPI + g is scored by lanes g * LPR + (i << SH) ...
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -244,64 +303,72 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   if (lane == 0) *ml = make_float2(m_run, l_tot);
 }
 
-// Cross-split combine: one wavefront per (batch entry, head).
+// Cross-split combine: one block of four wavefronts per (batch entry, head).
 // M = max_s m_s; out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// Lanes load the (max, sum) pairs of 64 splits at once; the partial vectors
-// are then read split by split with independent loads (D / 64 per lane).
+// Wave w accumulates splits w, w + 4, ... (lanes over the head dimension,
+// four splits' loads in flight); the four partial sums meet in LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int J = D / 64;
+  constexpr int U = 4;
+  __shared__ float red_max[4];
+  __shared__ float red_acc[4][D];
+  __shared__ float red_den[4];
   const int b = blockIdx.x / a.heads;
   const int h = blockIdx.x % a.heads;
   const int k0 = a.split_off[b];
   const int k1 = a.split_off[b + 1];
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   float mx = -INFINITY;
-  for (int k = k0 + lane; k < k1; k += 64) mx = fmaxf(mx, a.part_ml[(int64_t)k * a.heads + h].x);
+  for (int k = k0 + tid; k < k1; k += 256) mx = fmaxf(mx, a.part_ml[(int64_t)k * a.heads + h].x);
   mx = wave_max(mx);
+  if (lane == 0) red_max[w] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
   float den = 0.f;
   float acc[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) acc[j] = 0.f;
-  for (int kb = k0; kb < k1; kb += 64) {
-    const int k = kb + lane;
-    float wgt = 0.f;
-    if (k < k1) {
-      const float2 m_l = a.part_ml[(int64_t)k * a.heads + h];
-      // splits past the cache end carry (-inf, 0) and get weight 0
-      wgt = m_l.y > 0.f ? __builtin_amdgcn_exp2f(m_l.x - mx) : 0.f;
-      den = fmaf(wgt, m_l.y, den);
-    }
-    const int nk = min(64, k1 - kb);
-    int i = 0;
-    for (; i + 4 <= nk; i += 4) {
-      float wv[4], pv[4][J];
+  for (int kb = k0 + w; kb < k1; kb += 4 * U) {
+    float2 m_l[U];
+    float pv[U][J];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wv[u] = __shfl(wgt, i + u);
-        const float *po = a.part_o + ((int64_t)(kb + i + u) * a.heads + h) * D + lane;
+    for (int u = 0; u < U; ++u) {
+      const int k = kb + 4 * u;
+      if (k < k1) {
+        m_l[u] = a.part_ml[(int64_t)k * a.heads + h];
+        const float *po = a.part_o + ((int64_t)k * a.heads + h) * D + lane;
 #pragma unroll
         for (int j = 0; j < J; ++j) pv[u][j] = po[64 * j];
+      } else {
+        m_l[u] = make_float2(-INFINITY, 0.f);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-          if (wv[u] > 0.f) acc[j] = fmaf(wv[u], pv[u][j], acc[j]);
     }
-    for (; i < nk; ++i) {
-      const float wv = __shfl(wgt, i);
-      const float *po = a.part_o + ((int64_t)(kb + i) * a.heads + h) * D + lane;
 #pragma unroll
-      for (int j = 0; j < J; ++j)
-        if (wv > 0.f) acc[j] = fmaf(wv, po[64 * j], acc[j]);
+    for (int u = 0; u < U; ++u) {
+      // splits past the cache end carry (-inf, 0) and get weight 0
+      if (m_l[u].y > 0.f) {
+        const float wgt = __builtin_amdgcn_exp2f(m_l[u].x - mx);
+        den = fmaf(wgt, m_l[u].y, den);
+#pragma unroll
+        for (int j = 0; j < J; ++j) acc[j] = fmaf(wgt, pv[u][j], acc[j]);
+      }
     }
   }
-  den = wave_sum(den);
-  T *out = (T *)a.out + ((int64_t)b * a.heads + h) * D;
-  const float inv = 1.f / den;
 #pragma unroll
-  for (int j = 0; j < J; ++j) out[lane + 64 * j] = from_f<T>(acc[j] * inv);
+  for (int j = 0; j < J; ++j) red_acc[w][lane + 64 * j] = acc[j];
+  if (lane == 0) red_den[w] = den;
+  __syncthreads();
+  if (w != 0) return;
+  const float inv = 1.f / (red_den[0] + red_den[1] + red_den[2] + red_den[3]);
+  T *out = (T *)a.out + ((int64_t)b * a.heads + h) * D;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int d = lane + 64 * j;
+    out[d] = from_f<T>((red_acc[0][d] + red_acc[1][d] + red_acc[2][d] + red_acc[3][d]) * inv);
+  }
 }
 
 template <typename F>
@@ -322,10 +389,15 @@ hipError_t launch_decode_split(const DecodeArgs &a, int dtype, int head_dim, hip
     constexpr int D = decltype(dv)::value;
     const int64_t tasks = (int64_t)a.num_splits * a.heads;
     const dim3 grid((unsigned)((tasks + 3) / 4));
-    if (a.pool.table)
-      hipLaunchKernelGGL((decode_split_kernel<T, D, true>), grid, dim3(256), 0, s, a);
+    const bool fused = a.k_new != nullptr;
+    if (a.pool.table && fused)
+      hipLaunchKernelGGL((decode_split_kernel<T, D, true, true>), grid, dim3(256), 0, s, a);
+    else if (a.pool.table)
+      hipLaunchKernelGGL((decode_split_kernel<T, D, true, false>), grid, dim3(256), 0, s, a);
+    else if (fused)
+      hipLaunchKernelGGL((decode_split_kernel<T, D, false, true>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_split_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_split_kernel<T, D, false, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
   });
 }
@@ -335,7 +407,7 @@ hipError_t launch_decode_combine(const DecodeArgs &a, int dtype, int head_dim, h
   return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
     using T = decltype(tv);
     constexpr int D = decltype(dv)::value;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.n * a.heads), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.n * a.heads), dim3(256), 0, s, a);
     return hipGetLastError();
   });
 }

@@ -48,8 +48,8 @@ __global__ __launch_bounds__(64) void ring_write_kernel(RingWriteArgs a) {
     const float2 c = cs[i];
     const float x1 = to_f(kn[i]);
     const float x2 = to_f(kn[i + D / 2]);
-    K[i] = from_f<T>(x1 * c.x - x2 * c.y);
-    K[i + D / 2] = from_f<T>(x2 * c.x + x1 * c.y);
+    K[i] = from_f<T>(rope_lo(x1, x2, c));
+    K[i + D / 2] = from_f<T>(rope_hi(x1, x2, c));
     V[i] = vn[i];
     V[i + D / 2] = vn[i + D / 2];
   }
@@ -114,8 +114,8 @@ __global__ __launch_bounds__(256) void prefill_cache_write_kernel(PrefillArgs a)
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const float2 cc = cs[e];
-    r1[e] = from_f<T>(x1[e] * cc.x - x2[e] * cc.y);
-    r2[e] = from_f<T>(x2[e] * cc.x + x1[e] * cc.y);
+    r1[e] = from_f<T>(rope_lo(x1[e], x2[e], cc));
+    r2[e] = from_f<T>(rope_hi(x1[e], x2[e], cc));
   }
   T *K = (T *)a.pool.k + dst;
   T *V = (T *)a.pool.v + dst;

@@ -42,6 +42,7 @@ using namespace dev;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -232,19 +233,26 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
         for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       m_run = m_new;
     }
+    // The row sum adds the bf16-rounded weights, the same ones the PV
+    // product uses, so the output is an exact convex combination of V rows
+    // up to fp32 accumulation (v_dot2 against (1, 1) adds a rounded pair).
     float lsum = 0.f;
     bf16x8 pf[2][2];
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         f32x8 pv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 8; ++e)
           pv[e] = __builtin_amdgcn_exp2f(fmaf(s[j][8 * hh + e], qscale, -m_run));
-          lsum += pv[e];
-        }
         pf[j][hh] = __builtin_convertvector(pv, bf16x8);
+        const bf16x8 pb = pf[j][hh];
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, lsum, false);
       }
     l_run += lsum;
     // V^T operands read one MFMA step ahead of their use.

@@ -34,7 +34,7 @@ EXPORTED = (
     "rswa_abi_version", "rswa_workspace_bytes", "rswa_cache_init", "rswa_cache_destroy",
     "rswa_prefill", "rswa_set_batch", "rswa_ring_write", "rswa_decode_step",
     "rswa_advance", "rswa_get_state", "rswa_decode_plan", "rswa_status_string",
-    "rswa_last_error", "rswa_profile_enable", "rswa_profile_read",
+    "rswa_last_error", "rswa_profile_enable", "rswa_profile_read", "rswa_decode_step_fused",
 )
 RSWA_KERNEL_DECODE_SPLIT = 0
 RSWA_KERNEL_PREFILL_ATTENTION = 1
@@ -111,6 +111,7 @@ def load():
         "rswa_set_batch": (ctypes.c_int, [P, I32, pI32, P]),
         "rswa_ring_write": (ctypes.c_int, [P, I32, P, P, P]),
         "rswa_decode_step": (ctypes.c_int, [P, I32, P, P, P]),
+        "rswa_decode_step_fused": (ctypes.c_int, [P, I32, P, P, P, P, P]),
         "rswa_advance": (ctypes.c_int, [P, P]),
         "rswa_get_state": (ctypes.c_int, [P, I32, pI32, pI32, pI32, pI32, P]),
         "rswa_decode_plan": (ctypes.c_int, [P, pI32, pI32]),
@@ -184,6 +185,11 @@ def rswa_ring_write(handle, layer: int, k_new: int, v_new: int, stream: int) -> 
 
 def rswa_decode_step(handle, layer: int, q: int, out: int, stream: int) -> int:
     return load().rswa_decode_step(handle, layer, q, out, stream)
+
+
+def rswa_decode_step_fused(handle, layer: int, q: int, k_new: int, v_new: int, out: int,
+                           stream: int) -> int:
+    return load().rswa_decode_step_fused(handle, layer, q, k_new, v_new, out, stream)
 
 
 def rswa_advance(handle, stream: int) -> int:
@@ -329,6 +335,11 @@ class RSWACache:
         shp = (self.n, self.heads, self.head_dim)
         self._check(rswa_decode_step(self.handle, layer, self._ptr(q, shp), self._ptr(out, shp),
                                      self.stream()))
+
+    def decode_step_fused(self, layer: int, q, k_new, v_new, out):
+        shp = (self.n, self.heads, self.head_dim)
+        self._check(rswa_decode_step_fused(self.handle, layer, self._ptr(q, shp), self._ptr(k_new, shp),
+                                           self._ptr(v_new, shp), self._ptr(out, shp), self.stream()))
 
     def advance(self):
         self._check(rswa_advance(self.handle, self.stream()))

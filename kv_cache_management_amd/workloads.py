@@ -40,6 +40,13 @@ class Workload:
     # slot_table[slot_base + i], a shuffled permutation of the pool rows.
     paged: bool = False
     seed: int = 0
+    # Values (kinds 2 and 5) are drawn with std input_std * v_std_ratio.
+    v_std_ratio: float = 1.0
+
+    def std(self, kind: int) -> float:
+        """Standard deviation of the inputs of one kind (0-2 prefill Q/K/V,
+        3-5 decode Q/K/V)."""
+        return self.input_std * (self.v_std_ratio if kind in (2, 5) else 1.0)
 
     @property
     def batch(self) -> int:

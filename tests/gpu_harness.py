@@ -68,6 +68,8 @@ class Scenario:
     # Fill (layer, request) slices that are not checked with device-side
     # normals of the same distribution instead of host-drawn inputs.
     device_fill: bool = False
+    # Use rswa_decode_step_fused (ring write inside the decode kernel).
+    fused: bool = False
 
 
 class Inputs:
@@ -82,7 +84,7 @@ class Inputs:
         a = self.cache.get(key)
         if a is None or a.shape[0] < rows:
             a = synth.draw(self.w.seed, self.w.wid, layer, kind, req,
-                           (rows, self.w.heads, self.w.head_dim), self.w.input_std, self.w.dtype)
+                           (rows, self.w.heads, self.w.head_dim), self.w.std(kind), self.w.dtype)
             self.cache[key] = a
         return a[:rows]
 
@@ -122,15 +124,15 @@ def run_gpu(sc: Scenario, inputs: Inputs, record_state: bool = True):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234 + w.wid)
 
-    def filled(shape):
-        return torch.empty(shape, device="cuda", dtype=tdt).normal_(0.0, w.input_std, generator=gen)
+    def filled(shape, kind):
+        return torch.empty(shape, device="cuda", dtype=tdt).normal_(0.0, w.std(kind), generator=gen)
 
     def checked(l, r):
         return l in check_layers and r in check_reqs
 
     for l in layers:
         if sc.device_fill:
-            tq, tk, tv = (filled((int(offs[-1]), w.heads, w.head_dim)) for _ in range(3))
+            tq, tk, tv = (filled((int(offs[-1]), w.heads, w.head_dim), kind) for kind in range(3))
             for r in ids:
                 if checked(l, r) and w.prefill_lens[r]:
                     for t_, kind in ((tq, synth.Q_PREFILL), (tk, synth.K_PREFILL), (tv, synth.V_PREFILL)):
@@ -152,7 +154,7 @@ def run_gpu(sc: Scenario, inputs: Inputs, record_state: bool = True):
     for l in layers:
         for kind in range(3):
             if sc.device_fill:
-                t_ = filled((n, tmax, w.heads, w.head_dim))
+                t_ = filled((n, tmax, w.heads, w.head_dim), kind + 3)
                 for r in ids:
                     if checked(l, r):
                         t_[r, : total[r]] = to_torch(inputs.decode(l, kind, r, total[r]), w.dtype)
@@ -184,8 +186,11 @@ def run_gpu(sc: Scenario, inputs: Inputs, record_state: bool = True):
             kq, kk, kv = (dev[(l, kind)].view(n * tmax, w.heads, w.head_dim).index_select(0, idx)
                           for kind in range(3))
             o = outs[l][: len(active)]
-            cache.ring_write(l, kk.contiguous(), kv.contiguous())
-            cache.decode_step(l, kq.contiguous(), o)
+            if sc.fused:
+                cache.decode_step_fused(l, kq.contiguous(), kk.contiguous(), kv.contiguous(), o)
+            else:
+                cache.ring_write(l, kk.contiguous(), kv.contiguous())
+                cache.decode_step(l, kq.contiguous(), o)
         cache.advance()
         measured = step_idx - pre
         if measured in sc.check_steps:

@@ -247,7 +247,34 @@ static void test_step_machine_and_ring() {
   CHECK(HostState::cache_len(5, 20, 8) == 13);
   // request 0 (P = 100) reaches position 120 = max_positions after 20 steps
   CHECK(st.check_ring_write(0, &err) == RSWA_E_POSITION);
+  CHECK(st.check_fused(0, &err) == RSWA_E_POSITION);
   CHECK(st.request(0).t == 20);
+}
+
+// A fused ring write + decode counts as both calls for its layer.
+static void test_fused_step() {
+  Config c = resolved(base_cfg());
+  HostState st(c);
+  std::string err;
+  int32_t ids[1] = {1};
+  int32_t pl[1] = {7};
+  int64_t base[1] = {0};
+  register_all(st, 1, ids, pl, base);
+  st.commit_set_batch(1, ids, st.plan_decode(1, ids));
+  CHECK(st.check_fused(0, &err) == RSWA_OK);
+  st.commit_fused(0);
+  CHECK(st.check_fused(0, &err) == RSWA_E_STATE);
+  CHECK(st.check_decode(0, &err) == RSWA_E_STATE);
+  CHECK(st.check_ring_write(0, &err) == RSWA_E_STATE);
+  CHECK(st.check_advance(&err) == RSWA_E_STATE);  // layer 1 missing
+  CHECK(st.check_ring_write(1, &err) == RSWA_OK);
+  st.commit_ring_write(1);
+  CHECK(st.check_fused(1, &err) == RSWA_E_STATE);  // already written
+  CHECK(st.check_decode(1, &err) == RSWA_OK);
+  st.commit_decode(1);
+  CHECK(st.check_advance(&err) == RSWA_OK);
+  st.commit_advance();
+  CHECK(st.request(1).t == 1);
 }
 
 static void test_decode_plan() {
@@ -304,6 +331,7 @@ int main() {
   test_prefill_order_and_errors();
   test_prefill_xcd_plan();
   test_step_machine_and_ring();
+  test_fused_step();
   test_decode_plan();
   if (g_fail) {
     std::fprintf(stderr, "%d checks failed\n", g_fail);

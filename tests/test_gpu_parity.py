@@ -148,10 +148,14 @@ def test_single_page_bf16_every_step():
     _check_run(sc, res, inputs)
 
 
+# Q and K at std 1 give peaked softmax rows (a stress of masking and the
+# running max); V at half that keeps |out| below about 2, where rounding the
+# output to bf16 costs at most 2^-8 and the bf16 operands of the products
+# leave the rest of the 1e-2 absolute bound.
 SMALL_RAGGED = W.Workload(
     90, "small_ragged", layers=2, heads=3, head_dim=128, dtype="bf16",
     prefill_lens=(0, 1, 63, 64, 65, 300), window=16, decode_steps=60,
-    input_std=1.0, start_steps=(0, 3, 16, 17, 40, 5), paged=True)
+    input_std=1.0, start_steps=(0, 3, 16, 17, 40, 5), paged=True, v_std_ratio=0.5)
 
 
 @pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
@@ -203,3 +207,50 @@ def test_position_limit_is_reported_and_state_kept():
     assert e.value.status == RSWA_E_POSITION
     rp, cl, npos = cache.get_state([0, 1])
     assert list(npos) == [20, 30] and list(cl) == [14, 24]
+
+
+@pytest.mark.parametrize("dtype,head_dim,paged", [("bf16", 128, True), ("bf16", 128, False),
+                                                  ("bf16", 64, True), ("f32", 64, False)])
+def test_fused_ring_write_decode(dtype, head_dim, paged):
+    """rswa_decode_step_fused: oracle parity (outputs, state, pool rows) and
+    results identical to rswa_ring_write + rswa_decode_step."""
+    w = dataclasses.replace(SMALL_RAGGED, dtype=dtype, head_dim=head_dim, paged=paged,
+                            wid=140 + head_dim + (dtype == "f32") * 7 + paged)
+    inputs = H.Inputs(w)
+    sc = H.Scenario(w, steps=w.decode_steps, check_steps=range(w.decode_steps), fused=True)
+    res = H.run_gpu(sc, inputs)
+    _check_run(sc, res, inputs)
+    ref = H.run_gpu(dataclasses.replace(sc, fused=False), inputs, record_state=False)
+    for key, (g, out) in res["decode"].items():
+        g2, out2 = ref["decode"][key]
+        assert g == g2 and np.array_equal(out, out2), key
+    assert np.array_equal(res["cache"].v_pool.float().cpu().numpy(),
+                          ref["cache"].v_pool.float().cpu().numpy())
+    k1 = res["cache"].k_pool.float().cpu().numpy()
+    k2 = ref["cache"].k_pool.float().cpu().numpy()
+    assert np.array_equal(np.nan_to_num(k1, nan=7.0), np.nan_to_num(k2, nan=7.0))
+
+
+def test_fused_and_split_calls_share_state_rules():
+    from kv_cache_management_amd.rswa import RSWAError, RSWA_E_STATE
+    import torch
+
+    w = dataclasses.replace(SMALL_RAGGED, prefill_lens=(20, 30), start_steps=None, layers=2,
+                            wid=160, decode_steps=3)
+    sc = H.Scenario(w, steps=3, check_steps=[2], fused=True)
+    inputs = H.Inputs(w)
+    res = H.run_gpu(sc, inputs)
+    _check_run(sc, res, inputs)
+    cache = res["cache"]
+    z = torch.zeros((2, w.heads, w.head_dim), device="cuda", dtype=torch.bfloat16)
+    cache.ring_write(0, z, z)
+    with pytest.raises(RSWAError) as e:      # layer 0 already written this step
+        cache.decode_step_fused(0, z, z, z, z)
+    assert e.value.status == RSWA_E_STATE
+    cache.decode_step(0, z, z)
+    cache.decode_step_fused(1, z, z, z, z)
+    with pytest.raises(RSWAError):
+        cache.decode_step_fused(1, z, z, z, z)
+    cache.advance()
+    rp, cl, npos = cache.get_state([0, 1])
+    assert list(npos) == [24, 34]
