@@ -86,6 +86,8 @@ hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
 // bf16 MFMA causal prefill attention (128-row query tiles).
 bool prefill_mfma_supported(int dtype, int head_dim);
+// Query rows per block of the MFMA prefill kernel.
+int prefill_mfma_rows();
 hipError_t launch_prefill_mfma(const PrefillArgs &a, int head_dim, hipStream_t s);
 // Query-tile height the prefill attention kernel for (dtype, head_dim) uses.
 int prefill_tile_rows(int dtype, int head_dim);

@@ -244,7 +244,7 @@ hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_
 }
 
 int prefill_tile_rows(int dtype, int head_dim) {
-  return prefill_mfma_supported(dtype, head_dim) ? 128 : 64;
+  return prefill_mfma_supported(dtype, head_dim) ? prefill_mfma_rows() : 64;
 }
 
 hipError_t launch_prefill_attention(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s) {

@@ -5,9 +5,11 @@
 // section 2.1); the page's eager path computes it with a full-matrix softmax
 // (section 三).  Here it is a flash-attention forward: one block per (query
 // tile of 128 rows, head, request), 4 wavefronts of 32 query rows each, key
-// tiles of 64 streamed through double-buffered LDS, online softmax in base 2.
-// The loop is software-pipelined one tile deep: while the softmax of tile k
-// runs on the VALU, the scores of tile k + 1 run on the matrix cores.
+// tiles of 64 streamed through LDS (K and V tiles double-buffered apart, one
+// barrier per tile), online softmax in base 2.  The loop is software-
+// pipelined one tile deep: while the probabilities of tile k run on the
+// VALU, the scores of tile k + 1 run on the matrix cores, and P.V of tile k
+// runs beside the row max of tile k + 1.
 //
 // Per wavefront and key tile:
 //   S^T (64 keys x 32 queries) = K (64 x D) . Q^T (D x 32): A = K rows from
@@ -30,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -60,12 +63,6 @@ constexpr int kBN = 64;   // keys per tile
 #ifndef RSWA_PREFILL_MIN_BLOCKS
 #define RSWA_PREFILL_MIN_BLOCKS 2
 #endif
-// Issue priority of the matrix-core phases (0 = leave priorities alone).
-#ifndef RSWA_PREFILL_PRIO
-#define RSWA_PREFILL_PRIO 0
-#endif
-#define RSWA_PRIO_UP() do { if (RSWA_PREFILL_PRIO) __builtin_amdgcn_s_setprio(RSWA_PREFILL_PRIO); } while (0)
-#define RSWA_PRIO_DOWN() do { if (RSWA_PREFILL_PRIO) __builtin_amdgcn_s_setprio(0); } while (0)
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_kernel(PrefillArgs a) {
@@ -152,38 +149,52 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     rv = make_rsrc((const char *)a.pool.v + req_off, (uint32_t)kend * row_bytes);
   }
   const uint32_t col_off = (uint32_t)(h * D * 2 + (tid % CPR) * 16);
-  // Paged layout: slot-table entries of a tile are fetched one tile ahead of
-  // its key/value loads (rows_next), so the loads never wait on the table.
-  int32_t rows_next[KLD];
-  auto fetch_rows = [&](int k0) {
+  // Paged layout: pool rows of a tile's keys, fetched from the slot table a
+  // tile ahead of the loads that use them (-1 past kend).
+  int32_t rows_k[KLD], rows_v[KLD];
+  auto fetch_rows = [&](int32_t *rows, int k0) {
     if constexpr (PAGED) {
 #pragma unroll
       for (int it = 0; it < KLD; ++it) {
+        // Clamped index: an unconditional load keeps the loop body one
+        // basic block.
         const int j = k0 + (tid + 256 * it) / CPR;
-        rows_next[it] = j < kend ? table[base + j] : -1;
+        const int32_t row = table[base + min(j, kend - 1)];
+        rows[it] = j < kend ? row : -1;
       }
     }
   };
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int it = 0; it < KLD; ++it) {
-      const int j = k0 + (tid + 256 * it) / CPR;
-      uint32_t off;
-      if constexpr (PAGED)
-        off = rows_next[it] >= 0 ? (uint32_t)rows_next[it] * row_bytes + col_off : a.layer_bytes;
-      else
-        off = (uint32_t)j * row_bytes + col_off;
-      kreg[it] = buf_load16(rk, off);
-      vreg[it] = buf_load16(rv, off);
-    }
+  auto tile_off = [&](const int32_t *rows, int k0, int it) -> uint32_t {
+    if constexpr (PAGED)
+      return rows[it] >= 0 ? (uint32_t)rows[it] * row_bytes + col_off : a.layer_bytes;
+    else
+      return (uint32_t)(k0 + (tid + 256 * it) / CPR) * row_bytes + col_off;
   };
-  auto store_tile = [&](int buf) {
+  auto load_k = [&](int k0, const int32_t *rows) {
+#pragma unroll
+    for (int it = 0; it < KLD; ++it) kreg[it] = buf_load16(rk, tile_off(rows, k0, it));
+  };
+  auto load_v = [&](int k0, const int32_t *rows) {
+#pragma unroll
+    for (int it = 0; it < KLD; ++it) vreg[it] = buf_load16(rv, tile_off(rows, k0, it));
+  };
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < KLD; ++it) {
       const int idx = tid + 256 * it;
       *(uint4 *)(lk[buf] + (idx / CPR) * KP + (idx % CPR) * 8) = kreg[it];
+    }
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < KLD; ++it) {
+      const int idx = tid + 256 * it;
       *(uint4 *)(lv[buf] + (idx / CPR) * VP + (idx % CPR) * 8) = vreg[it];
     }
+  };
+  auto shift_rows = [&]() {
+#pragma unroll
+    for (int it = 0; it < KLD; ++it) rows_v[it] = rows_k[it];
   };
   // Transposing-read address of this lane: in its 16-lane group, lane
   // 4e + q points at key (4g + e), dims (16 * (group & 1) + 4q) of a 32-dim
@@ -191,9 +202,8 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
   const int tp = lane & 15;
   const int vtr = (4 * g + (tp >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (tp & 3);
 
-  // S^T = K . Q^T for the tile in LDS buffer `buf`, two 32-key blocks.
+  // S^T = K . Q^T for the key tile in K buffer `buf`, two 32-key blocks.
   auto scores = [&](int buf, f32x16 *s) {
-    RSWA_PRIO_UP();
     const f32x16 zero = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -202,11 +212,11 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
         const bf16x8 ka = *(const bf16x8 *)(lk[buf] + (32 * j + (lane & 31)) * KP + 16 * ks + 8 * g);
         s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? zero : s[j], 0, 0, 0);
       }
-    RSWA_PRIO_DOWN();
   };
-  // Online softmax of tile k0's scores and O^T += V^T . P^T from buffer `buf`.
-  auto softmax_pv = [&](f32x16 *s, int buf, int k0, bool may_mask) {
-    if (may_mask && k0 + kBN - 1 > q0) {  // causal mask on tiles that reach the diagonal
+  // Row max of the scores of tile k0 (lane's query column), after the causal
+  // mask on tiles that reach this wave's diagonal.
+  auto mask_max = [&](f32x16 *s, int k0, bool may_mask) -> float {
+    if (may_mask && k0 + kBN - 1 > q0) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -220,7 +230,11 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+  // Raises the running max when a row's max grows by more than 8 (log2
+  // units), rescaling its sum and output.
+  auto rescale = [&](float mx) {
     const float m_cand = mx * qscale;
     const bool grow = m_cand > m_run + 8.f;
     if (__any(grow)) {
@@ -233,95 +247,112 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
         for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       m_run = m_new;
     }
-    // The row sum adds the bf16-rounded weights, the same ones the PV
-    // product uses, so the output is an exact convex combination of V rows
-    // up to fp32 accumulation (v_dot2 against (1, 1) adds a rounded pair).
-    float lsum = 0.f;
-    bf16x8 pf[2][2];
-    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+  };
+  // Probabilities of the 8 keys (j, hh) of each query column as the bf16
+  // B operand.  The row sum adds the bf16-rounded weights, the same ones the
+  // PV product uses, so the output is an exact convex combination of V rows
+  // up to fp32 accumulation (v_dot2 against (1, 1) adds a rounded pair).
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+  auto probs = [&](const f32x16 *s, int j, int hh, float &lsum) -> bf16x8 {
+    f32x8 pv;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int e = 0; e < 8; ++e)
+      pv[e] = __builtin_amdgcn_exp2f(fmaf(s[j][8 * hh + e], qscale, -m_run));
+    const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, lsum, false);
+    return pb;
+  };
+  // O^T += V^T . P^T over the 16 keys (j, hh) of the V tile in buffer `buf`.
+  auto pv_block = [&](int buf, int j, int hh, bf16x8 pb) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f32x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(s[j][8 * hh + e], qscale, -m_run));
-        pf[j][hh] = __builtin_convertvector(pv, bf16x8);
-        const bf16x8 pb = pf[j][hh];
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, lsum, false);
-      }
-    l_run += lsum;
-    // V^T operands read one MFMA step ahead of their use.
-    RSWA_PRIO_UP();
-    auto v_operand = [&](int step) -> bf16x8 {
-      const int d = step / 4, j = (step / 2) % 2, hh = step % 2;
+    for (int d = 0; d < DB; ++d) {
       const bf16 *p0 = lv[buf] + vtr + (32 * j + 16 * hh) * VP + 32 * d;
       const bf16x4 lo = lds_read_tr4(p0);
       const bf16x4 hi = lds_read_tr4(p0 + 8 * VP);
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    bf16x8 va = v_operand(0);
-#pragma unroll
-    for (int step = 0; step < 4 * DB; ++step) {
-      const bf16x8 vnext = step + 1 < 4 * DB ? v_operand(step + 1) : va;
-      const int d = step / 4, j = (step / 2) % 2, hh = step % 2;
-      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[j][hh], o[d], 0, 0, 0);
-      va = vnext;
+      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[d], 0, 0, 0);
     }
-    RSWA_PRIO_DOWN();
   };
 
-  // Tile k lives in LDS buffer k & 1; tile k + 1 is staged from registers at
-  // the top of iteration k and tile k + 2 is fetched into registers meanwhile.
+  // Pipeline.  K tiles and V tiles are double-buffered separately: K(k) in
+  // lk[k & 1], V(k) in lv[k & 1].  At the top of step k the LDS holds K(k+1)
+  // and V(k); registers hold K(k+2) and V(k+1) (loaded a step earlier) and
+  // the masked scores and row max of tile k.  Step k:
+  //   barrier (every wave is done with step k-1, so K(k) and V(k-1) are free)
+  //   rescale if tile k raises the running max
+  //   scores of tile k+1 on the matrix cores, probabilities of tile k on the
+  //   VALU (interleaved)
+  //   store K(k+2) -> lk[k & 1], V(k+1) -> lv[(k+1) & 1]; load V(k+2), K(k+3)
+  //   P.V of tile k on the matrix cores, row max of tile k+1 on the VALU
   // A wave takes part in tile k only if k * kBN <= its last query row.
   const int last_q = q0 + 31;
-  f32x16 s_cur[2], s_nxt[2];
-  fetch_rows(0);
-  load_tile(0);
-  store_tile(0);
-  fetch_rows(kBN);
-  if (ntile > 1) load_tile(kBN);
-  fetch_rows(2 * kBN);
+  auto tile_step = [&](auto steady_c, int k, f32x16 *sc, f32x16 *sn, float mx_cur, float &mx_nxt) {
+    constexpr bool kSteady = decltype(steady_c)::value;
+    __syncthreads();
+    const bool act = kSteady || k * kBN <= last_q;
+    const bool act_n = kSteady || (k + 1 < ntile && (k + 1) * kBN <= last_q);
+    if (act) rescale(mx_cur);
+    if (act_n) scores((k + 1) & 1, sn);
+    float lsum = 0.f;
+    bf16x8 p00, p01, p10, p11;
+    if (act) {
+      p00 = probs(sc, 0, 0, lsum);
+      p01 = probs(sc, 0, 1, lsum);
+      p10 = probs(sc, 1, 0, lsum);
+    }
+    if (kSteady || k + 2 < ntile) store_k(k & 1);
+    if (kSteady || k + 1 < ntile) store_v((k + 1) & 1);
+    if (kSteady || k + 2 < ntile) load_v((k + 2) * kBN, rows_v);
+    if (kSteady || k + 3 < ntile) load_k((k + 3) * kBN, rows_k);
+    shift_rows();
+    fetch_rows(rows_k, (k + 4) * kBN);
+    if (act) {
+      pv_block(k & 1, 0, 0, p00);
+      pv_block(k & 1, 0, 1, p01);
+      pv_block(k & 1, 1, 0, p10);
+      p11 = probs(sc, 1, 1, lsum);
+      pv_block(k & 1, 1, 1, p11);
+      l_run += lsum;
+    }
+    if (act_n) mx_nxt = mask_max(sn, (k + 1) * kBN, !kSteady);
+  };
+
+  // Prologue: K(0), V(0), K(1) into LDS; V(1), K(2) loading; rows of tiles
+  // 2 and 3 fetched; scores and row max of tile 0 (every wave takes part).
+  f32x16 sA[2], sB[2];
+  float mxA = -INFINITY, mxB = -INFINITY;
+  fetch_rows(rows_k, 0);
+  load_k(0, rows_k);
+  load_v(0, rows_k);
+  fetch_rows(rows_v, kBN);
+  store_k(0);
+  store_v(0);
+  load_k(kBN, rows_v);
+  load_v(kBN, rows_v);
+  fetch_rows(rows_k, 2 * kBN);
+  store_k(1);
+  load_k(2 * kBN, rows_k);
+  shift_rows();
+  fetch_rows(rows_k, 3 * kBN);
   __syncthreads();
-  scores(0, s_cur);
-  // Steady state: tiles kt and kt + 1 lie wholly below the block's first
-  // query row (no mask, every wave takes part) and tile kt + 2 exists, so the
-  // body has no branch and the scores of kt + 1 can interleave with the
-  // softmax of kt.
-  const int steady = max(0, min(ntile - 2, 2 * qt - 1));
+  scores(0, sA);
+  mxA = mask_max(sA, 0, true);
+
+  // Steady state (pairs of steps): tiles k and k + 1 lie wholly below the
+  // block's first query row (no mask, every wave takes part) and tile k + 2
+  // exists.  The two steps of a pair swap the score registers.
+  const int steady = max(0, min(ntile - 2, 2 * qt - 1)) & ~1;
   int kt = 0;
-  for (; kt < steady; ++kt) {
-    const int cur = kt & 1;
-    __syncthreads();
-    store_tile(cur ^ 1);
-    __syncthreads();
-    load_tile((kt + 2) * kBN);
-    fetch_rows((kt + 3) * kBN);
-    scores(cur ^ 1, s_nxt);
-    softmax_pv(s_cur, cur, kt * kBN, false);
-    s_cur[0] = s_nxt[0];
-    s_cur[1] = s_nxt[1];
+  for (; kt < steady; kt += 2) {
+    tile_step(std::true_type{}, kt, sA, sB, mxA, mxB);
+    tile_step(std::true_type{}, kt + 1, sB, sA, mxB, mxA);
   }
-  for (; kt < ntile; ++kt) {
-    const int cur = kt & 1;
-    __syncthreads();  // every wave is done with tile kt - 1 (buffer cur ^ 1)
-    if (kt + 1 < ntile) store_tile(cur ^ 1);
-    __syncthreads();
-    if (kt + 2 < ntile) {
-      load_tile((kt + 2) * kBN);
-      fetch_rows((kt + 3) * kBN);
-    }
-    const bool next = kt + 1 < ntile && (kt + 1) * kBN <= last_q;
-    if (next) scores(cur ^ 1, s_nxt);
-    if (kt * kBN <= last_q) softmax_pv(s_cur, cur, kt * kBN, true);
-    if (next) {
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
-    }
+  for (; kt < ntile; kt += 2) {
+    tile_step(std::false_type{}, kt, sA, sB, mxA, mxB);
+    if (kt + 1 < ntile) tile_step(std::false_type{}, kt + 1, sB, sA, mxB, mxA);
   }
 
   if (qi >= p_len) return;
@@ -339,11 +370,14 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     }
 }
 
+
 }  // namespace
 
 bool prefill_mfma_supported(int dtype, int head_dim) {
   return dtype == RSWA_DTYPE_BF16 && (head_dim == 64 || head_dim == 128);
 }
+
+int prefill_mfma_rows() { return kBM; }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, int head_dim, hipStream_t s) {
   if (a.num_tiles == 0) return hipSuccess;
