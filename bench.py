@@ -117,6 +117,18 @@ class Job:
         self.kv_launches = L * decode_steps
         ev = lambda: torch.cuda.Event(enable_timing=True)
         self.ev = {k: ev() for k in ("p0", "p1", "d0", "d1")}
+        self.step_ev = None
+        self.scratch = None
+
+    def enable_step_events(self, cold: bool):
+        """One event pair around every measured decode step; with cold, a
+        1 GiB scratch write before each step (outside its pair) evicts the
+        L2 and the 256 MB infinity cache."""
+        torch = self.torch
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        self.step_ev = [(ev(), ev()) for _ in range(self.steps)]
+        if cold:
+            self.scratch = torch.empty(1 << 30, dtype=torch.uint8, device=self.dec.device)
 
     def _check(self, st):
         if st != 0:
@@ -171,15 +183,33 @@ class Job:
             self._set_batch(list(range(n)))
         self.ev["d0"].record(self.stream)
         lib.rswa_profile_enable(h, 1 if profile_kernels else 0)
-        for i in range(self.steps):
-            self._step(self.pre + i, n)
+        if self.step_ev is None:
+            for i in range(self.steps):
+                self._step(self.pre + i, n)
+        else:
+            for i in range(self.steps):
+                if self.scratch is not None:
+                    self.scratch.fill_(i & 255)
+                a, b = self.step_ev[i]
+                a.record(self.stream)
+                self._step(self.pre + i, n)
+                b.record(self.stream)
         lib.rswa_profile_enable(h, 0)
         self.ev["d1"].record(self.stream)
 
     def times_ms(self):
+        """(prefill ms, decode ms) of the last run; decode is one bracket
+        around all measured steps, or with the cold protocol the sum of the
+        per-step pairs (the scratch writes between them excluded)."""
         e = self.ev
         e["d1"].synchronize()
-        return e["p0"].elapsed_time(e["p1"]), e["d0"].elapsed_time(e["d1"])
+        dec = e["d0"].elapsed_time(e["d1"])
+        if self.scratch is not None:
+            dec = float(sum(self.step_times_ms()))
+        return e["p0"].elapsed_time(e["p1"]), dec
+
+    def step_times_ms(self):
+        return [a.elapsed_time(b) for a, b in self.step_ev]
 
     def kernel_time(self, kernel):
         st, ms, cnt = self.R.rswa_profile_read(self.h, kernel, self.sptr)
@@ -203,6 +233,57 @@ def traffic_from_profile(workload: str):
     if not rec or rec.get("kernel_source_sha256_16") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def measured_peaks(torch, rswa, read_gib: int = 4):
+    """What this GPU reaches on its own: a streaming read of a 4 GiB buffer
+    with the decode kernel's load instruction (rswa_measure_read), and a
+    large bf16 GEMM through the vendor library (torch.matmul -> hipBLASLt)."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    stream = torch.cuda.current_stream(dev)
+    nbytes = read_gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(7)
+    sink = torch.empty(rswa.RSWA_MEASURE_SINK_WORDS, dtype=torch.int32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        st = rswa.rswa_measure_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
+        assert st == 0, st
+    a, b = ev(), ev()
+    reps = 10
+    a.record(stream)
+    for _ in range(reps):
+        rswa.rswa_measure_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
+    b.record(stream)
+    b.synchronize()
+    read_gbs = nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
+    del buf
+    n = 8192
+    x = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    y = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        z = torch.matmul(x, y)
+    a.record(stream)
+    reps = 20
+    for _ in range(reps):
+        z = torch.matmul(x, y)
+    b.record(stream)
+    b.synchronize()
+    gemm_tflops = 2 * n ** 3 * reps / (a.elapsed_time(b) / 1e3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(read_gbs, 1), "hbm_read": f"rswa_measure_read over {read_gib} GiB",
+            "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
+            "bf16_gemm": f"torch.matmul {n}x{n}x{n} bf16"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(w: W.Workload, budget_s: float = 16.0):
@@ -267,6 +348,7 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0):
         "sample": (f"fp64 numpy oracle (RingCache.step): {steps_done} steady-state decode steps of "
                    f"requests {reqs} in layer {layer} ({kv / 1e9:.3f} GB of algorithmic KV reads "
                    f"in {t_dec:.2f} s); prefill: one request, first {p} tokens, layer {layer}"),
+        "cpu": cpu_model(),
         "decode_steps_per_s_per_request_layer": round(steps_done / t_dec, 3),
         "prefill_gflops": round(pf_flops / t_pf / 1e9, 3),
     }
@@ -285,6 +367,13 @@ def main():
                          "rswa_decode_step_fused")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="do not time kernels with event pairs inside the timed steps")
+    ap.add_argument("--cold", action="store_true",
+                    help="cold-cache protocol: a 1 GiB scratch write before every measured "
+                         "decode step, outside that step's event pair")
+    ap.add_argument("--no-step-times", action="store_true",
+                    help="no per-step event pairs (no step-time percentiles)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured read / GEMM peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -317,6 +406,8 @@ def main():
     log(f"workload {w.name}: {w.batch} requests x {w.layers} layers, sum P = {sum(w.prefill_lens)}, "
         f"{steps} decode steps")
     job = Job(w, steps, fused=not args.unfused)
+    if args.cold or not args.no_step_times:
+        job.enable_step_events(cold=args.cold)
     torch.cuda.synchronize()
     for i in range(args.warmup):
         t0 = time.perf_counter()
@@ -335,6 +426,15 @@ def main():
         log(f"step {i}: prefill {a:.2f} ms, decode {b:.2f} ms")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_stats = None
+    if job.step_ev is not None:
+        st_ms = np.array(job.step_times_ms())
+        q = max(1, len(st_ms) // 4)
+        step_stats = {"p50_ms": round(float(np.percentile(st_ms, 50)), 4),
+                      "p99_ms": round(float(np.percentile(st_ms, 99)), 4),
+                      "max_ms": round(float(st_ms.max()), 4),
+                      "last_quarter_over_first_quarter": round(float(st_ms[-q:].mean() / st_ms[:q].mean()), 4),
+                      "steps": int(len(st_ms)), "run": "last measured job"}
     k_dec = job.kernel_time(rswa.RSWA_KERNEL_DECODE_SPLIT) if prof else (None, 0)
     k_pf = job.kernel_time(rswa.RSWA_KERNEL_PREFILL_ATTENTION) if prof else (None, 0)
 
@@ -386,10 +486,21 @@ def main():
         "decode_ms_per_step": round(dec_s * 1e3 / (steps * args.steps), 4),
         "prefill_tflops": round(pf_tflops, 2),
         "prefill_mfma_frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "decode_cache": "cold (1 GiB scratch write before each step)" if args.cold else "warm",
+        "decode_step_times": step_stats,
         "roofline": roofline,
         "prefill_kernel": prefill_kernel,
+        "measured_peak": None,
         "cpu_baseline": None,
     }
+    if not args.no_peaks:
+        log("measuring the read and GEMM peaks")
+        mp = measured_peaks(torch, rswa)
+        out["measured_peak"] = mp
+        if roofline:
+            roofline["frac_of_measured_read"] = round(roofline["achieved"] / mp["hbm_read_GBps"], 4)
+        if prefill_kernel:
+            prefill_kernel["frac_of_measured_gemm"] = round(prefill_kernel["achieved"] / mp["bf16_gemm_TFLOPs"], 4)
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

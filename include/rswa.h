@@ -193,6 +193,17 @@ int rswa_profile_enable(rswa_cache *c, int enable);
 int rswa_profile_read(rswa_cache *c, int32_t kernel, double *total_ms, int64_t *launches,
                       void *stream);
 
+/* Measurement helper, not part of the attention path: reads `bytes` of
+ * device memory at `buf` with the decode kernel's 16-byte non-temporal
+ * loads, 4096 blocks of 256 threads, each block one contiguous chunk, and
+ * writes one word per block to `sink` (device, at least 4096 uint32), so
+ * that the bytes / kernel time it reaches is the read rate the decode
+ * kernel's HBM figure can be set against.  Asynchronous on `stream`.
+ * Errors: RSWA_E_ARG (null pointer or zero bytes), RSWA_E_UNSUPPORTED
+ * (bytes of 16 TiB or more), RSWA_E_HIP (launch failure). */
+enum { RSWA_MEASURE_SINK_WORDS = 4096 };
+int rswa_measure_read(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
+
 /* Static name of a status code. */
 const char *rswa_status_string(int status);
 

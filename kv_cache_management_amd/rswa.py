@@ -35,7 +35,9 @@ EXPORTED = (
     "rswa_prefill", "rswa_set_batch", "rswa_ring_write", "rswa_decode_step",
     "rswa_advance", "rswa_get_state", "rswa_decode_plan", "rswa_status_string",
     "rswa_last_error", "rswa_profile_enable", "rswa_profile_read", "rswa_decode_step_fused",
+    "rswa_measure_read",
 )
+RSWA_MEASURE_SINK_WORDS = 4096
 RSWA_KERNEL_DECODE_SPLIT = 0
 RSWA_KERNEL_PREFILL_ATTENTION = 1
 
@@ -120,6 +122,7 @@ def load():
         "rswa_profile_enable": (ctypes.c_int, [P, ctypes.c_int]),
         "rswa_profile_read": (ctypes.c_int, [P, I32, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(ctypes.c_int64), P]),
+        "rswa_measure_read": (ctypes.c_int, [P, ctypes.c_uint64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -224,6 +227,12 @@ def rswa_profile_read(handle, kernel: int, stream: int):
     n = ctypes.c_int64()
     st = load().rswa_profile_read(handle, kernel, ctypes.byref(ms), ctypes.byref(n), stream)
     return st, ms.value, n.value
+
+
+def rswa_measure_read(buf: int, nbytes: int, sink: int, stream: int) -> int:
+    """Streaming read of nbytes at device address buf (sink: device buffer of
+    RSWA_MEASURE_SINK_WORDS uint32)."""
+    return load().rswa_measure_read(buf, nbytes, sink, stream)
 
 
 def rswa_status_string(status: int) -> str:

@@ -108,3 +108,11 @@ def test_null_handle_calls(R):
     assert R.rswa_decode_step(None, 0, 1, 1, 0) == R.RSWA_E_ARG
     assert R.rswa_advance(None, 0) == R.RSWA_E_ARG
     assert R.rswa_cache_destroy(None) == R.RSWA_OK
+
+
+def test_measure_read_rejects_bad_arguments(R):
+    # validated before any device work
+    assert R.rswa_measure_read(None, 1 << 20, 1, None) == R.RSWA_E_ARG
+    assert R.rswa_measure_read(1, 0, 1, None) == R.RSWA_E_ARG
+    assert R.rswa_measure_read(1, 1 << 20, None, None) == R.RSWA_E_ARG
+    assert R.rswa_measure_read(1, 1 << 45, 1, None) == R.RSWA_E_UNSUPPORTED
