@@ -276,6 +276,37 @@ def measured_peaks(torch, rswa, read_gib: int = 4):
             "bf16_gemm": f"torch.matmul {n}x{n}x{n} bf16"}
 
 
+def ngram_ban_timing(torch, rswa, requests=64, vocab=129280, ngram=35, window=128, reps=200):
+    """Time of one rswa_ngram_ban call at the page's sizes: 64 requests,
+    129,280-token vocabulary, n = 35 inside a 128-token window, bf16 logits.
+    Token rows repeat a short block so bans occur.  The kernel reads each
+    window (512 B per request) and writes only the banned logits: it is
+    launch-latency bound, so the figure reported is microseconds per call."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    stride = 512
+    period = torch.randint(1, 61, (requests, 1), device=dev, generator=g)
+    block = torch.randint(0, vocab, (requests, 64), device=dev, generator=g)
+    idx = torch.arange(stride, device=dev)[None, :] % period
+    tokens = torch.gather(block, 1, idx).to(torch.int32).contiguous()
+    lengths = torch.randint(ngram, stride + 1, (requests,), device=dev, generator=g).to(torch.int32)
+    logits = torch.randn((requests, vocab), device=dev, generator=g).to(torch.bfloat16)
+    for _ in range(5):
+        rswa.ngram_ban(tokens, lengths, logits, ngram=ngram, window=window)
+    stream = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        rswa.ngram_ban(tokens, lengths, logits, ngram=ngram, window=window)
+    b.record(stream)
+    b.synchronize()
+    banned = int(torch.isneginf(logits.float()).sum().item())
+    return {"avg_us_per_call": round(a.elapsed_time(b) * 1e3 / reps, 2), "requests": requests,
+            "vocab": vocab, "ngram": ngram, "window": window, "logits": "bf16",
+            "banned_entries": banned, "bound": "launch latency"}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -490,9 +521,11 @@ def main():
         "decode_step_times": step_stats,
         "roofline": roofline,
         "prefill_kernel": prefill_kernel,
+        "ngram_ban": None,
         "measured_peak": None,
         "cpu_baseline": None,
     }
+    out["ngram_ban"] = ngram_ban_timing(torch, rswa)
     if not args.no_peaks:
         log("measuring the read and GEMM peaks")
         mp = measured_peaks(torch, rswa)

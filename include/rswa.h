@@ -193,6 +193,31 @@ int rswa_profile_enable(rswa_cache *c, int enable);
 int rswa_profile_read(rswa_cache *c, int32_t kernel, double *total_ms, int64_t *launches,
                       void *stream);
 
+/* Windowed no-repeat n-gram ban on decode logits [page section 2.3: the
+ * anti-loop processor looks for repeats only inside a sliding window of
+ * recent tokens and sets to -inf every token that would reproduce an n-gram
+ * of `ngram` tokens found there; defaults ngram = 35, window = 128].
+ * Independent of any cache handle.
+ *   tokens   device int32 [n][token_stride]: row r holds request r's token
+ *            sequence; only its first lengths[r] entries count (lengths
+ *            outside [0, token_stride] are clamped into it).
+ *   lengths  device int32 [n].
+ *   logits   device [n][vocab], RSWA_DTYPE_BF16 or RSWA_DTYPE_F32, updated
+ *            in place: for a sequence x_0 .. x_{L-1}, every n-gram x_i ..
+ *            x_{i+ngram-1} with max(0, L - window) <= i <= L - ngram whose
+ *            first ngram - 1 tokens equal the last ngram - 1 tokens of the
+ *            sequence bans x_{i+ngram-1}: logits[r][x] = -inf.  Nothing is
+ *            banned when L < ngram or window < ngram; tokens outside
+ *            [0, vocab) are skipped.  Other logits are not touched.
+ * The caller owns every buffer; asynchronous on `stream`.
+ * Errors: RSWA_E_ARG (n < 0, ngram < 1, window < 1, vocab < 1, negative
+ * token_stride, unknown dtype, null pointer with n > 0), RSWA_E_UNSUPPORTED
+ * (window > RSWA_NGRAM_MAX_WINDOW), RSWA_E_HIP (launch failure). */
+enum { RSWA_NGRAM_MAX_WINDOW = 4096 };
+int rswa_ngram_ban(const int32_t *tokens, int64_t token_stride, const int32_t *lengths, int32_t n,
+                   int32_t ngram, int32_t window, void *logits, int64_t vocab, int32_t dtype,
+                   void *stream);
+
 /* Measurement helper, not part of the attention path: reads `bytes` of
  * device memory at `buf` with the decode kernel's 16-byte non-temporal
  * loads, 4096 blocks of 256 threads, each block one contiguous chunk, and

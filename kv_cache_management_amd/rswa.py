@@ -35,8 +35,9 @@ EXPORTED = (
     "rswa_prefill", "rswa_set_batch", "rswa_ring_write", "rswa_decode_step",
     "rswa_advance", "rswa_get_state", "rswa_decode_plan", "rswa_status_string",
     "rswa_last_error", "rswa_profile_enable", "rswa_profile_read", "rswa_decode_step_fused",
-    "rswa_measure_read",
+    "rswa_measure_read", "rswa_ngram_ban",
 )
+RSWA_NGRAM_MAX_WINDOW = 4096
 RSWA_MEASURE_SINK_WORDS = 4096
 RSWA_KERNEL_DECODE_SPLIT = 0
 RSWA_KERNEL_PREFILL_ATTENTION = 1
@@ -123,6 +124,8 @@ def load():
         "rswa_profile_read": (ctypes.c_int, [P, I32, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(ctypes.c_int64), P]),
         "rswa_measure_read": (ctypes.c_int, [P, ctypes.c_uint64, P, P]),
+        "rswa_ngram_ban": (ctypes.c_int, [P, ctypes.c_int64, P, I32, I32, I32, P, ctypes.c_int64,
+                                          I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -233,6 +236,37 @@ def rswa_measure_read(buf: int, nbytes: int, sink: int, stream: int) -> int:
     """Streaming read of nbytes at device address buf (sink: device buffer of
     RSWA_MEASURE_SINK_WORDS uint32)."""
     return load().rswa_measure_read(buf, nbytes, sink, stream)
+
+
+def rswa_ngram_ban(tokens: int, token_stride: int, lengths: int, n: int, ngram: int, window: int,
+                   logits: int, vocab: int, dtype: int, stream: int) -> int:
+    """Windowed no-repeat n-gram ban on device logits (raw device addresses)."""
+    return load().rswa_ngram_ban(tokens, token_stride, lengths, n, ngram, window, logits, vocab,
+                                 dtype, stream)
+
+
+def ngram_ban(tokens, lengths, logits, ngram: int = 35, window: int = 128):
+    """Torch front end: tokens int32 [n][stride], lengths int32 [n], logits
+    bf16/f32 [n][vocab], all on the current CUDA device; bans in place."""
+    import torch
+
+    for name, t in (("tokens", tokens), ("lengths", lengths), ("logits", logits)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if tokens.dtype != torch.int32 or lengths.dtype != torch.int32:
+        raise ValueError("tokens and lengths must be int32")
+    if logits.dim() != 2 or tokens.dim() != 2 or lengths.shape != (tokens.shape[0],) \
+            or logits.shape[0] != tokens.shape[0]:
+        raise ValueError("shapes: tokens [n][stride], lengths [n], logits [n][vocab]")
+    dt = {torch.bfloat16: RSWA_DTYPE_BF16, torch.float32: RSWA_DTYPE_F32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bf16 or f32")
+    st = rswa_ngram_ban(tokens.data_ptr(), tokens.shape[1], lengths.data_ptr(), tokens.shape[0],
+                        ngram, window, logits.data_ptr(), logits.shape[1], dt,
+                        torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RSWAError(st, f"rswa_ngram_ban: {status_name(st)}")
+    return logits
 
 
 def rswa_status_string(status: int) -> str:

@@ -116,3 +116,24 @@ def test_measure_read_rejects_bad_arguments(R):
     assert R.rswa_measure_read(1, 0, 1, None) == R.RSWA_E_ARG
     assert R.rswa_measure_read(1, 1 << 20, None, None) == R.RSWA_E_ARG
     assert R.rswa_measure_read(1, 1 << 45, 1, None) == R.RSWA_E_UNSUPPORTED
+
+
+def test_ngram_ban_rejects_bad_arguments(R):
+    ok = dict(tokens=1, token_stride=128, lengths=1, n=4, ngram=35, window=128, logits=1,
+              vocab=129280, dtype=R.RSWA_DTYPE_BF16, stream=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return R.rswa_ngram_ban(a["tokens"], a["token_stride"], a["lengths"], a["n"], a["ngram"],
+                                a["window"], a["logits"], a["vocab"], a["dtype"], a["stream"])
+
+    assert call(n=-1) == R.RSWA_E_ARG
+    assert call(ngram=0) == R.RSWA_E_ARG
+    assert call(window=0) == R.RSWA_E_ARG
+    assert call(vocab=0) == R.RSWA_E_ARG
+    assert call(token_stride=-1) == R.RSWA_E_ARG
+    assert call(dtype=7) == R.RSWA_E_ARG
+    assert call(tokens=None) == R.RSWA_E_ARG
+    assert call(logits=None) == R.RSWA_E_ARG
+    assert call(window=R.RSWA_NGRAM_MAX_WINDOW + 1) == R.RSWA_E_UNSUPPORTED
+    assert call(n=0, tokens=None, lengths=None, logits=None) == R.RSWA_OK  # nothing to do
