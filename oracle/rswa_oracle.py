@@ -214,13 +214,26 @@ def decode_mask(prefill_len: int, s: int, window: int) -> np.ndarray:
     return (j < prefill_len) | (j >= first_gen)
 
 
+def swa_decode_mask(prefill_len: int, s: int, window: int) -> np.ndarray:
+    """Baseline: a standard sliding window [T5 §2.1, the contrast it draws].
+
+    The query of step s sees the newest W logical positions of 0 .. P+s,
+    prefill and generated alike (the current one included), so once the
+    window has moved past the prefill its keys are gone.  Reading: the
+    window is applied at decode; prefill attention stays causal.
+    """
+    n = prefill_len + s + 1
+    return np.arange(n) >= n - window
+
+
 def decode_logical(q_s, k_hist, v_hist, prefill_len: int, s: int, window: int,
-                   base: float = 10000.0, scale=None) -> np.ndarray:
+                   base: float = 10000.0, scale=None, mode: str = "rswa") -> np.ndarray:
     """Output of decode step s from the full history, masked explicitly.
 
     q_s: [H, D] unrotated query of step s.
     k_hist, v_hist: [P+s+1, H, D] unrotated keys / values of logical
     positions 0 .. P+s (prefill tokens, then generated tokens 0 .. s).
+    mode "rswa" uses decode_mask, "swa" the standard-window baseline.
     Returns [H, D].
     """
     k_hist = np.asarray(k_hist, dtype=np.float64)
@@ -232,7 +245,8 @@ def decode_logical(q_s, k_hist, v_hist, prefill_len: int, s: int, window: int,
     pos = np.arange(n)
     k_hat = rope(k_hist, pos[:, None], base)
     q_hat = rope(np.asarray(q_s, dtype=np.float64), position(prefill_len, s), base)
-    mask = decode_mask(prefill_len, s, window)[None, :]
+    mask_fn = {"rswa": decode_mask, "swa": swa_decode_mask}[mode]
+    mask = mask_fn(prefill_len, s, window)[None, :]
     return np.stack(
         [masked_attention(q_hat[None, h], k_hat[:, h], v_hist[:, h], mask, sc)[0]
          for h in range(n_heads)],
@@ -284,11 +298,15 @@ class RingCache:
         self.owner[slot] = self.s
         return slot
 
-    def attend(self, q) -> np.ndarray:
-        """Attention of the current step's query over the valid cache rows."""
+    def attend(self, q, mode: str = "rswa") -> np.ndarray:
+        """Attention of the current step's query over the valid cache rows:
+        all of them (R-SWA), or for the standard-window baseline only the
+        ring and the prefill rows at positions >= P + s + 1 - W."""
         n_valid = cache_len(self.P, self.s, self.W)
         q_hat = rope(np.asarray(q, dtype=np.float64), position(self.P, self.s), self.base)
         mask = np.ones((1, n_valid), dtype=bool)
+        if mode == "swa":
+            mask[0, : max(0, min(self.P, self.P + self.s + 1 - self.W))] = False
         return np.stack(
             [masked_attention(q_hat[None, h], self.K[:n_valid, h], self.V[:n_valid, h],
                               mask, self.scale)[0]
@@ -296,10 +314,10 @@ class RingCache:
             axis=0,
         )
 
-    def step(self, q, k_new, v_new) -> np.ndarray:
+    def step(self, q, k_new, v_new, mode: str = "rswa") -> np.ndarray:
         """One decode step: write, attend, advance.  Returns [H, D]."""
         self.write(k_new, v_new)
-        out = self.attend(q)
+        out = self.attend(q, mode)
         self.s += 1
         return out
 

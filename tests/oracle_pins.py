@@ -346,6 +346,59 @@ def pin_planted_keys(O):
             assert dist > 0.1, (target, dist)
 
 
+# ------------------------------------------- standard-window baseline (SWA)
+
+def pin_swa_is_textbook_band(O):
+    """The standard-window baseline: query at position i sees keys
+    i - W < j <= i over prefill and generated tokens alike; checked for the
+    logical and the physical form against banded SDPA in fp64."""
+    for p_len, w, n in ((9, 4, 20), (0, 3, 11), (5, 12, 14), (30, 7, 9)):
+        h, d = 2, 8
+        pq, pk, pv, dq, dk, dv = _run_decode(O, p_len, w, n, h, d, 40 + p_len + w)
+        q = np.concatenate([pq, dq])
+        k = np.concatenate([pk, dk])
+        v = np.concatenate([pv, dv])
+        tot = p_len + n
+        pos = np.arange(tot, dtype=np.float64)[:, None]
+        i = np.arange(tot)[:, None]
+        j = np.arange(tot)[None, :]
+        band = (j <= i) & (i - j < w)
+        want = _sdpa(complex_rope(q, pos, _freqs(d)), complex_rope(k, pos, _freqs(d)), v,
+                     1 / math.sqrt(d), mask=band)
+        rc = O.RingCache(p_len, w, h, d)
+        rc.load_prefill(pk, pv)
+        for st in range(n):
+            got_l = O.decode_logical(dq[st], k[: p_len + st + 1], v[: p_len + st + 1], p_len, st, w,
+                                     mode="swa")
+            got_p = rc.step(dq[st], dk[st], dv[st], mode="swa")
+            assert np.allclose(got_l, want[p_len + st], atol=1e-12), ("logical", p_len, w, st)
+            assert np.allclose(got_p, want[p_len + st], atol=1e-12), ("physical", p_len, w, st)
+
+
+def pin_swa_visible_set(O):
+    """q = 0 with one-hot values: the output is the indicator of the visible
+    positions divided by their number; the baseline sees exactly the last
+    min(W, P + s + 1) positions, a subset of what R-SWA sees."""
+    p_len, w, n, d = 11, 4, 20, 64
+    eye = np.eye(d)
+    k_all = _rng(5, 9).standard_normal((p_len + n, 1, d))
+    v_all = eye[: p_len + n][:, None, :]
+    rc = O.RingCache(p_len, w, 1, d)
+    rc.load_prefill(k_all[:p_len], v_all[:p_len])
+    for st in range(n):
+        last = p_len + st
+        vis = list(range(max(0, last - w + 1), last + 1))
+        want = np.zeros(d)
+        want[vis] = 1.0 / len(vis)
+        got = O.decode_logical(np.zeros((1, d)), k_all[: last + 1], v_all[: last + 1], p_len, st, w,
+                               mode="swa")[0]
+        assert np.allclose(got, want, atol=1e-15), ("logical", st)
+        got_p = rc.step(np.zeros((1, d)), k_all[last], v_all[last], mode="swa")[0]
+        assert np.allclose(got_p, want, atol=1e-15), ("physical", st)
+        assert set(np.flatnonzero(O.swa_decode_mask(p_len, st, w))) <= \
+            set(np.flatnonzero(O.decode_mask(p_len, st, w)))
+
+
 # ------------------------------------------------------------- work counts
 
 def pin_work_counts(O):

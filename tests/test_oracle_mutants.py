@@ -78,7 +78,24 @@ def _masked_attention_axis0(q, k, v, mask, scale):
     return p @ np.asarray(v, dtype=np.float64)
 
 
+_orig_attend = O.RingCache.attend
+
+
+def _attend_swa_lo_shift(self, q, mode="rswa"):
+    if mode != "swa":
+        return _orig_attend(self, q, mode)
+    n_valid = O.cache_len(self.P, self.s, self.W)
+    q_hat = O.rope(np.asarray(q, dtype=np.float64), O.position(self.P, self.s), self.base)
+    mask = np.ones((1, n_valid), dtype=bool)
+    mask[0, : max(0, min(self.P, self.P + self.s + 2 - self.W))] = False
+    return np.stack([O.masked_attention(q_hat[None, h], self.K[:n_valid, h], self.V[:n_valid, h],
+                                        mask, self.scale)[0] for h in range(q_hat.shape[0])], axis=0)
+
+
 MUTANTS = {
+    "swa_window_one_too_wide": {"swa_decode_mask": lambda p, s, w: np.arange(p + s + 1) >= p + s - w},
+    "swa_keeps_prefill": {"swa_decode_mask": lambda p, s, w: _orig["decode_mask"](p, s, w)},
+    "swa_physical_window_start_shifted": {"RingCache.attend": _attend_swa_lo_shift},
     "rope_sign": {"rope": _rope_sign},
     "rope_shifted_position": {"rope": _rope_shift},
     "rope_interleaved_pairs": {"rope": _rope_interleaved},
