@@ -67,6 +67,18 @@ enum {
 
 enum { RSWA_DTYPE_BF16 = 0, RSWA_DTYPE_F32 = 1 };
 
+/* Which keys a decode step attends to.
+ *   RSWA_ATTENTION_RSWA: the method [page section 2.1]: every prefill key
+ *     plus the newest min(t + 1, W) generated keys.
+ *   RSWA_ATTENTION_SWA: the baseline the same section contrasts it with, a
+ *     standard sliding window that also cuts the prefill keys: only the
+ *     newest W logical positions, P + t + 1 - W .. P + t, prefill and
+ *     generated alike.  The cache layout, prefill and ring writes are the
+ *     same; prefill attention stays causal.
+ * A growing full cache is RSWA_ATTENTION_RSWA with W at least the number of
+ * decode steps (the ring never wraps). */
+enum { RSWA_ATTENTION_RSWA = 0, RSWA_ATTENTION_SWA = 1 };
+
 typedef struct rswa_config {
   int32_t num_layers;     /* >= 1 */
   int32_t num_heads;      /* >= 1; key/value heads = query heads */
@@ -82,7 +94,8 @@ typedef struct rswa_config {
                                  rswa_prefill call; 0 means 262144 */
   int32_t decode_split_tokens; /* keys per split-KV work item, a multiple
                                   of 64; 0 means chosen per batch */
-  int32_t reserved0;
+  int32_t attention;      /* RSWA_ATTENTION_RSWA (0) or the baseline
+                             RSWA_ATTENTION_SWA (1), see below */
   double rope_base;       /* > 0; 0 means 10000 */
   double softmax_scale;   /* <= 0 means 1/sqrt(head_dim) */
   const int32_t *slot_table; /* device int32[slot_table_len] of pool rows,

@@ -35,6 +35,7 @@ int resolve_config(const rswa_config &in, Config *out, std::string *err) {
   c.max_prefill_tokens =
       in.max_prefill_tokens == 0 ? kDefaultMaxPrefillTokens : in.max_prefill_tokens;
   c.decode_split_tokens = in.decode_split_tokens;
+  c.attention = in.attention;
   c.rope_base = in.rope_base == 0 ? 10000.0 : in.rope_base;
   c.softmax_scale = in.softmax_scale > 0 ? in.softmax_scale : 0.0;
   c.has_table = in.slot_table != nullptr;
@@ -62,6 +63,8 @@ int resolve_config(const rswa_config &in, Config *out, std::string *err) {
     return fail(err, RSWA_E_ARG, "max_prefill_tokens must be in [1, 2^31]");
   if (c.decode_split_tokens < 0 || c.decode_split_tokens % kSplitQuantum != 0)
     return fail(err, RSWA_E_ARG, "decode_split_tokens must be a non-negative multiple of 64");
+  if (c.attention != RSWA_ATTENTION_RSWA && c.attention != RSWA_ATTENTION_SWA)
+    return fail(err, RSWA_E_ARG, "attention must be RSWA_ATTENTION_RSWA or RSWA_ATTENTION_SWA");
   if (!(c.rope_base > 0) || !std::isfinite(c.rope_base))
     return fail(err, RSWA_E_ARG, "rope_base must be positive");
   if (!std::isfinite(in.softmax_scale)) return fail(err, RSWA_E_ARG, "softmax_scale must be finite");
@@ -305,11 +308,13 @@ int HostState::check_set_batch(int32_t n, const int32_t *ids, std::string *err) 
 
 DecodePlan HostState::plan_decode(int32_t n, const int32_t *ids) const {
   DecodePlan p;
-  // Longest cache a request reaches while decoding: prefill_len + W.
+  // Key range a request's decode steps can reach: logical slots
+  // decode_key0(P) .. P + W - 1 (all of 0 .. P + W - 1 for R-SWA).
   std::vector<int64_t> lmax(n);
   int64_t sum = 0;
   for (int b = 0; b < n; ++b) {
-    lmax[b] = (int64_t)req_[ids[b]].plen + cfg_.window;
+    const int32_t p = req_[ids[b]].plen;
+    lmax[b] = (int64_t)p + cfg_.window - decode_key0(p);
     sum += lmax[b];
   }
   int64_t s;

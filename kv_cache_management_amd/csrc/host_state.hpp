@@ -9,6 +9,7 @@
 // cache never exceeds prefill_len + W rows.
 #pragma once
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 #include <string>
@@ -40,7 +41,7 @@ inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a
 struct Config {
   int32_t num_layers = 0, num_heads = 0, head_dim = 0, window = 0;
   int32_t max_positions = 0, max_requests = 0, dtype = 0, max_splits = 0;
-  int32_t decode_split_tokens = 0;
+  int32_t decode_split_tokens = 0, attention = 0;
   int64_t num_slots = 0, max_prefill_tokens = 0, slot_table_len = 0;
   double rope_base = 0, softmax_scale = 0;
   bool has_table = false;
@@ -140,7 +141,11 @@ class HostState {
   // Plans the packed offsets and the query tiles (of `tile` rows) of a
   // checked prefill call.
   PrefillPlan plan_prefill(int32_t n, const int32_t *plen, int32_t tile) const;
-  // Work of a causal query tile: number of key tiles it covers.
+  // First logical slot any decode step of a request with prefill_len p may
+  // attend to: 0, or with the standard-window baseline p - W + 1.
+  int32_t decode_key0(int32_t p) const {
+    return cfg_.attention == RSWA_ATTENTION_SWA ? std::max(0, p - cfg_.window + 1) : 0;
+  }
 
   int check_set_batch(int32_t n, const int32_t *ids, std::string *err) const;
   DecodePlan plan_decode(int32_t n, const int32_t *ids) const;

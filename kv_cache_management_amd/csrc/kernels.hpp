@@ -56,6 +56,7 @@ struct DecodeArgs {
   float qscale;               // softmax_scale * log2(e)
   uint32_t layer_bytes;       // bytes of one layer of a pool (< 2^32)
   int32_t n, heads, window, layer, num_splits, split_tokens;
+  int32_t attention;          // RSWA_ATTENTION_RSWA or RSWA_ATTENTION_SWA
 };
 
 struct PrefillArgs {

@@ -419,6 +419,7 @@ int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, 
   a.layer = layer;
   a.num_splits = plan.num_splits();
   a.split_tokens = plan.split_tokens;
+  a.attention = c->cfg.attention;
   hipStream_t s = (hipStream_t)stream;
   const int pi = c->prof_begin(RSWA_KERNEL_DECODE_SPLIT, s);
   hipError_t e = rswa::launch_decode_split(a, c->cfg.dtype, c->cfg.head_dim, s);

@@ -116,13 +116,20 @@ __global__ __launch_bounds__(256, RSWA_DECODE_MIN_BLOCKS) void decode_split_kern
   const int t = a.st.t[r];
   const int64_t base = a.st.base[r];
   const int L = p_len + min(t + 1, a.window);
-  const int start = s * a.split_tokens;
+  // Keys lo .. L-1 are visible: all of them for R-SWA; with the standard
+  // window only logical positions P + t + 1 - W .. P + t.  Splits tile the
+  // range from key0, the lowest lo any step of this request can have.
+  const bool swa = a.attention == RSWA_ATTENTION_SWA;
+  const int key0 = swa ? max(0, p_len - a.window + 1) : 0;
+  const int lo = swa ? min(p_len, max(0, p_len + t + 1 - a.window)) : 0;
+  const int split0 = key0 + s * a.split_tokens;
+  const int start = max(split0, lo);
+  const int end = min(split0 + a.split_tokens, L);
   float2 *ml = a.part_ml + (int64_t)ks * a.heads + h;
-  if (start >= L) {
+  if (start >= end) {
     if (lane == 0) *ml = make_float2(-INFINITY, 0.f);
     return;
   }
-  const int end = min(start + a.split_tokens, L);
   const int g = lane / LPR;
   const int c = lane % LPR;
 

@@ -29,6 +29,8 @@ RSWA_E_STATE = -5
 RSWA_E_HIP = -6
 RSWA_DTYPE_BF16 = 0
 RSWA_DTYPE_F32 = 1
+RSWA_ATTENTION_RSWA = 0
+RSWA_ATTENTION_SWA = 1
 
 EXPORTED = (
     "rswa_abi_version", "rswa_workspace_bytes", "rswa_cache_init", "rswa_cache_destroy",
@@ -56,7 +58,7 @@ class rswa_config(ctypes.Structure):
         ("max_splits", ctypes.c_int32),
         ("max_prefill_tokens", ctypes.c_int64),
         ("decode_split_tokens", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("attention", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
         ("softmax_scale", ctypes.c_double),
         ("slot_table", ctypes.c_void_p),
@@ -293,6 +295,7 @@ class RSWACache:
                  softmax_scale: float = 0.0, slot_table: Optional[np.ndarray] = None,
                  max_prefill_tokens: int = 0, max_splits: int = 0,
                  decode_split_tokens: int = 0, pool_fill: Optional[float] = None,
+                 attention: str = "rswa",
                  device: str = "cuda"):
         import torch
 
@@ -315,6 +318,9 @@ class RSWACache:
         cfg.max_splits = max_splits
         cfg.max_prefill_tokens = max_prefill_tokens
         cfg.decode_split_tokens = decode_split_tokens
+        if attention not in ("rswa", "swa"):
+            raise ValueError("attention must be 'rswa' or 'swa'")
+        cfg.attention = RSWA_ATTENTION_SWA if attention == "swa" else RSWA_ATTENTION_RSWA
         cfg.rope_base = rope_base
         cfg.softmax_scale = softmax_scale
         shape = (num_layers, num_slots, num_heads, head_dim)

@@ -70,6 +70,8 @@ class Scenario:
     device_fill: bool = False
     # Use rswa_decode_step_fused (ring write inside the decode kernel).
     fused: bool = False
+    # "rswa", or "swa" for the standard-window baseline.
+    attention: str = "rswa"
 
 
 class Inputs:
@@ -116,7 +118,8 @@ def run_gpu(sc: Scenario, inputs: Inputs, record_state: bool = True):
                       rope_base=w.rope_base, slot_table=table,
                       max_prefill_tokens=max(1, sum(w.prefill_lens)),
                       decode_split_tokens=sc.split_tokens,
-                      pool_fill=float("nan") if sc.poison else None)
+                      pool_fill=float("nan") if sc.poison else None,
+                      attention=sc.attention)
     ids = list(range(n))
     res = {"prefill": {}, "decode": {}, "state": [], "cache": cache}
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -216,7 +219,8 @@ def oracle_prefill(w: Workload, inputs: Inputs, layer: int, req: int, rows=None)
     return O.prefill(q, k, v, w.rope_base, None, rows)
 
 
-def oracle_decode(w: Workload, inputs: Inputs, layer: int, req: int, gen_indices: Sequence[int]):
+def oracle_decode(w: Workload, inputs: Inputs, layer: int, req: int, gen_indices: Sequence[int],
+                  mode: str = "rswa"):
     """Oracle outputs at the given generated indices of one (layer, request),
     through the physical ring (attention computed only where asked)."""
     p_len = w.prefill_lens[req]
@@ -232,7 +236,7 @@ def oracle_decode(w: Workload, inputs: Inputs, layer: int, req: int, gen_indices
     for s in range(last + 1):
         rc.write(dk[s], dv[s])
         if s in wanted:
-            want[s] = rc.attend(dq[s])
+            want[s] = rc.attend(dq[s], mode)
         rc.s += 1
     return want, rc
 

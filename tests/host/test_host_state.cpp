@@ -323,6 +323,26 @@ static void test_decode_plan() {
   register_all(st3, 64, ids.data(), pl.data(), base.data());
   CHECK(st3.check_set_batch(64, ids.data(), &err) == RSWA_OK);
   CHECK(st3.plan_decode(64, ids.data()).num_splits() <= 100);
+  // Standard-window baseline: splits tile P - W + 1 .. P + W - 1 only.
+  rc.attention = RSWA_ATTENTION_SWA;
+  rc.decode_split_tokens = 64;
+  rc.max_splits = 0;
+  Config c4 = resolved(rc);
+  HostState st4(c4);
+  register_all(st4, 64, ids.data(), pl.data(), base.data());
+  CHECK(st4.check_set_batch(64, ids.data(), &err) == RSWA_OK);
+  DecodePlan p4 = st4.plan_decode(64, ids.data());
+  for (int i = 0; i < 64; ++i) {
+    CHECK(st4.decode_key0(pl[i]) == pl[i] - 127);
+    CHECK(p4.split_off[i + 1] - p4.split_off[i] == (2 * 128 - 1 + 63) / 64);
+  }
+  // a short prompt: the window reaches back to slot 0
+  CHECK(st4.decode_key0(50) == 0);
+  CHECK(st.decode_key0(5000) == 0);  // R-SWA: every prefill key
+  rc.attention = 2;
+  rswa_config bad = rc;
+  Config out;
+  CHECK(resolve_config(bad, &out, &err) == RSWA_E_ARG);
 }
 
 int main() {

@@ -76,6 +76,7 @@ def _cfg(R, **kw):
     ("max_requests", 0, "max_requests"),
     ("decode_split_tokens", 65, "multiple of 64"),
     ("slot_table_len", 3, "slot_table_len"),
+    ("attention", 2, "attention"),
 ])
 def test_workspace_bytes_rejects_bad_config(R, field, value, needle):
     assert R.rswa_workspace_bytes(_cfg(R, **{field: value})) == 0

@@ -60,7 +60,7 @@ def _check_run(sc: H.Scenario, res, inputs: H.Inputs, check_pool: bool = True):
         by_lr.setdefault((l, r), []).append((g, out))
     assert by_lr, "no decode outputs recorded"
     for (l, r), items in sorted(by_lr.items()):
-        want, _ = H.oracle_decode(w, inputs, l, r, [g for g, _ in items])
+        want, _ = H.oracle_decode(w, inputs, l, r, [g for g, _ in items], sc.attention)
         for g, out in items:
             H.compare(out, want[g], w.dtype, f"decode layer {l} req {r} gen {g}")
     # ring state, bit-exact against the closed forms
@@ -254,3 +254,39 @@ def test_fused_and_split_calls_share_state_rules():
     cache.advance()
     rp, cl, npos = cache.get_state([0, 1])
     assert list(npos) == [24, 34]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("dtype,head_dim,paged", [("bf16", 128, True), ("bf16", 64, False),
+                                                  ("f32", 128, False)])
+def test_standard_window_baseline(dtype, head_dim, paged, fused):
+    """RSWA_ATTENTION_SWA: decode sees only the newest W positions (prefill
+    keys older than that are cut); ragged prompts shorter and longer than W,
+    warm-up and wrapped ring phases, forced small splits so that several
+    splits per request start below the window."""
+    w = dataclasses.replace(SMALL_RAGGED, dtype=dtype, head_dim=head_dim, paged=paged,
+                            wid=170 + head_dim + (dtype == "f32") * 3 + paged)
+    inputs = H.Inputs(w)
+    for split in (0, 64):
+        sc = H.Scenario(w, steps=w.decode_steps, check_steps=range(w.decode_steps), fused=fused,
+                        attention="swa", split_tokens=split)
+        res = H.run_gpu(sc, inputs)
+        _check_run(sc, res, inputs)
+
+
+def test_standard_window_differs_from_rswa():
+    """Sanity of the contrast: once the window has left the prefill the two
+    modes disagree, before that (and for P = 0) they agree."""
+    w = dataclasses.replace(SMALL_RAGGED, prefill_lens=(0, 40), start_steps=None, layers=1, wid=190,
+                            decode_steps=40, window=16)
+    inputs = H.Inputs(w)
+    out = {}
+    for mode in ("rswa", "swa"):
+        sc = H.Scenario(w, steps=w.decode_steps, check_steps=range(w.decode_steps), attention=mode)
+        out[mode] = H.run_gpu(sc, inputs, record_state=False)["decode"]
+    for (step, l, r), (g, o) in out["rswa"].items():
+        o2 = out["swa"][(step, l, r)][1]
+        same = np.array_equal(o, o2)
+        p_len = w.prefill_lens[r]
+        cut = p_len > 0 and p_len + g + 1 > w.window   # some prefill key left the window
+        assert same != cut, (r, g)
