@@ -18,6 +18,7 @@ values, L = prefill_len + min(t + 1, W).  Prefill TFLOP/s counts
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import json
 import os
@@ -42,11 +43,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kv_bytes_per_layer_step(w: W.Workload, t_before):
+def visible_keys(p: int, t: int, window: int, attention: str = "rswa") -> int:
+    """Keys the decode step of a request with prefill p and t generated
+    tokens before it attends to: P + min(t + 1, W) for R-SWA, the newest
+    min(W, P + t + 1) positions for the standard-window baseline."""
+    if attention == "swa":
+        return min(window, p + t + 1)
+    return p + min(t + 1, window)
+
+
+def kv_bytes_per_layer_step(w: W.Workload, t_before, attention: str = "rswa"):
     """Algorithmic K+V bytes one layer's decode reads for the active requests,
     given each request's generated count before the step."""
     eb = w.elem_bytes
-    return sum(2 * w.heads * w.head_dim * eb * (p + min(t + 1, w.window))
+    return sum(2 * w.heads * w.head_dim * eb * visible_keys(p, t, w.window, attention)
                for p, t in zip(w.prefill_lens, t_before))
 
 
@@ -57,7 +67,8 @@ def prefill_flops(w: W.Workload):
 class Job:
     """Device-resident inputs and the cache for one workload."""
 
-    def __init__(self, w: W.Workload, decode_steps: int, seed: int = 0, fused: bool = True):
+    def __init__(self, w: W.Workload, decode_steps: int, seed: int = 0, fused: bool = True,
+                 attention: str = "rswa"):
         import torch
         from kv_cache_management_amd import rswa
 
@@ -73,7 +84,7 @@ class Job:
         self.cache = rswa.RSWACache(L, H, D, w.window, max_requests=n, num_slots=w.pool_rows(),
                                     dtype=w.dtype, max_positions=w.max_positions,
                                     rope_base=w.rope_base, slot_table=w.slot_table(),
-                                    max_prefill_tokens=sum(w.prefill_lens))
+                                    max_prefill_tokens=sum(w.prefill_lens), attention=attention)
         self.h = self.cache.handle
         gen = torch.Generator(device=dev)
         gen.manual_seed(seed)
@@ -113,7 +124,7 @@ class Job:
         # measured-step KV bytes (all layers)
         self.kv_bytes = 0
         for s in range(decode_steps):
-            self.kv_bytes += L * kv_bytes_per_layer_step(w, [st + s for st in starts])
+            self.kv_bytes += L * kv_bytes_per_layer_step(w, [st + s for st in starts], attention)
         self.kv_launches = L * decode_steps
         ev = lambda: torch.cuda.Event(enable_timing=True)
         self.ev = {k: ev() for k in ("p0", "p1", "d0", "d1")}
@@ -317,7 +328,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(w: W.Workload, budget_s: float = 16.0):
+def cpu_baseline(w: W.Workload, budget_s: float = 16.0, attention: str = "rswa"):
     """The oracle, as it stands, timed on this host's cores on a bounded sample
     of the same workload (decode of sampled requests in steady state)."""
     from kv_cache_management_amd import synth
@@ -356,8 +367,8 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0):
         t0 = time.perf_counter()
         for i in range(nmax):
             s = s0 + i
-            rc.step(dq[s], dk[s], dv[s])
-            kv += 2 * w.heads * w.head_dim * w.elem_bytes * O.cache_len(p, s, w.window)
+            rc.step(dq[s], dk[s], dv[s], attention)
+            kv += 2 * w.heads * w.head_dim * w.elem_bytes * visible_keys(p, s, w.window, attention)
             steps_done += 1
             if time.perf_counter() - t0 > per_req_budget:
                 break
@@ -398,6 +409,11 @@ def main():
                          "rswa_decode_step_fused")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="do not time kernels with event pairs inside the timed steps")
+    ap.add_argument("--attention", choices=("rswa", "swa"), default="rswa",
+                    help="swa: the standard sliding-window baseline (prefill keys cut)")
+    ap.add_argument("--window", type=int, default=None,
+                    help="override the workload's W (a W of at least the decode steps is the "
+                         "growing full-cache baseline)")
     ap.add_argument("--cold", action="store_true",
                     help="cold-cache protocol: a 1 GiB scratch write before every measured "
                          "decode step, outside that step's event pair")
@@ -434,9 +450,11 @@ def main():
 
     w = W.ALL[args.workload]
     steps = args.decode_steps or w.decode_steps
+    if args.window:
+        w = dataclasses.replace(w, window=args.window)
     log(f"workload {w.name}: {w.batch} requests x {w.layers} layers, sum P = {sum(w.prefill_lens)}, "
         f"{steps} decode steps")
-    job = Job(w, steps, fused=not args.unfused)
+    job = Job(w, steps, fused=not args.unfused, attention=args.attention)
     if args.cold or not args.no_step_times:
         job.enable_step_events(cold=args.cold)
     torch.cuda.synchronize()
@@ -461,7 +479,11 @@ def main():
     if job.step_ev is not None:
         st_ms = np.array(job.step_times_ms())
         q = max(1, len(st_ms) // 4)
+        # step time against output length: median of 16 steps around each mark
+        marks = sorted(set(int(x) for x in np.linspace(0, len(st_ms) - 1, 5)))
+        by_t = {str(m): round(float(np.median(st_ms[max(0, m - 8): m + 8])), 4) for m in marks}
         step_stats = {"p50_ms": round(float(np.percentile(st_ms, 50)), 4),
+                      "ms_at_measured_step": by_t,
                       "p99_ms": round(float(np.percentile(st_ms, 99)), 4),
                       "max_ms": round(float(st_ms.max()), 4),
                       "last_quarter_over_first_quarter": round(float(st_ms[-q:].mean() / st_ms[:q].mean()), 4),
@@ -511,7 +533,10 @@ def main():
                    "prefill_tokens": sum(w.prefill_lens),
                    "kv_layout": "page-size-1 slot table" if w.paged else "contiguous",
                    "decode_call": "rswa_ring_write + rswa_decode_step" if args.unfused
-                   else "rswa_decode_step_fused"},
+                   else "rswa_decode_step_fused",
+                   "attention": "standard sliding window (baseline)" if args.attention == "swa"
+                   else ("R-SWA" if w.window < steps + max(w.starts()) else
+                         "growing full cache (W >= generated tokens)")},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_steps_per_s": round(steps * args.steps / dec_s, 2),
         "decode_ms_per_step": round(dec_s * 1e3 / (steps * args.steps), 4),
@@ -536,7 +561,7 @@ def main():
             prefill_kernel["frac_of_measured_gemm"] = round(prefill_kernel["achieved"] / mp["bf16_gemm_TFLOPs"], 4)
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
         log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.attention)
     job.cache.close()
     print(json.dumps(out), flush=True)
 
