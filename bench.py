@@ -130,6 +130,18 @@ class Job:
         self.ev = {k: ev() for k in ("p0", "p1", "d0", "d1")}
         self.step_ev = None
         self.scratch = None
+        self.graph_k = 0
+        self.graph = None
+
+    def enable_graph(self, k: int):
+        """Measured decode steps replay one captured graph of k whole steps
+        (every layer's fused decode, then advance).  Each replay reuses the
+        inputs of the first k measured steps; the kernels read and advance
+        the per-request state on the device, so positions and ring slots move
+        on as in eager steps."""
+        if self.steps % k:
+            raise ValueError(f"decode steps ({self.steps}) must be a multiple of --graph {k}")
+        self.graph_k = k
 
     def enable_step_events(self, cold: bool):
         """One event pair around every measured decode step; with cold, a
@@ -192,6 +204,9 @@ class Job:
             self._step(g, len(act))
         if current != list(range(n)):
             self._set_batch(list(range(n)))
+        if self.graph_k:
+            self._run_graph()
+            return
         self.ev["d0"].record(self.stream)
         lib.rswa_profile_enable(h, 1 if profile_kernels else 0)
         if self.step_ev is None:
@@ -206,6 +221,38 @@ class Job:
                 self._step(self.pre + i, n)
                 b.record(self.stream)
         lib.rswa_profile_enable(h, 0)
+        self.ev["d1"].record(self.stream)
+
+    def _run_graph(self):
+        torch, lib, h = self.torch, self.lib, self.h
+        k = self.graph_k
+        first_free = False
+        if self.graph is None:
+            # capture on a side stream; the capture calls count as enqueuing
+            # the first replay's k steps
+            self.graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(self.stream)
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(self.graph, stream=side):
+                    sptr = side.cuda_stream
+                    L = self.w.layers
+                    for i in range(k):
+                        g = self.pre + i
+                        for l in range(L):
+                            blk = self.dec_ptr0 + ((g * L + l) * 3) * self.row_bytes
+                            self._check(lib.rswa_decode_step_fused(
+                                h, l, blk, blk + self.row_bytes, blk + 2 * self.row_bytes,
+                                self.out_ptr[l], sptr))
+                        self._check(lib.rswa_advance(h, sptr))
+            self.stream.wait_stream(side)
+            first_free = True
+        self.ev["d0"].record(self.stream)
+        for j in range(self.steps // k):
+            if not first_free:
+                self._check(lib.rswa_note_steps(h, k))
+            first_free = False
+            self.graph.replay()
         self.ev["d1"].record(self.stream)
 
     def times_ms(self):
@@ -414,6 +461,9 @@ def main():
     ap.add_argument("--window", type=int, default=None,
                     help="override the workload's W (a W of at least the decode steps is the "
                          "growing full-cache baseline)")
+    ap.add_argument("--graph", type=int, default=0, metavar="K",
+                    help="replay a captured graph of K whole decode steps (fused call; the "
+                         "graph reuses the first K steps' inputs)")
     ap.add_argument("--cold", action="store_true",
                     help="cold-cache protocol: a 1 GiB scratch write before every measured "
                          "decode step, outside that step's event pair")
@@ -455,7 +505,11 @@ def main():
     log(f"workload {w.name}: {w.batch} requests x {w.layers} layers, sum P = {sum(w.prefill_lens)}, "
         f"{steps} decode steps")
     job = Job(w, steps, fused=not args.unfused, attention=args.attention)
-    if args.cold or not args.no_step_times:
+    if args.graph:
+        if args.unfused or args.cold:
+            sys.exit("--graph captures fused steps with warm caches only")
+        job.enable_graph(args.graph)
+    elif args.cold or not args.no_step_times:
         job.enable_step_events(cold=args.cold)
     torch.cuda.synchronize()
     for i in range(args.warmup):
@@ -533,7 +587,8 @@ def main():
                    "prefill_tokens": sum(w.prefill_lens),
                    "kv_layout": "page-size-1 slot table" if w.paged else "contiguous",
                    "decode_call": "rswa_ring_write + rswa_decode_step" if args.unfused
-                   else "rswa_decode_step_fused",
+                   else (f"rswa_decode_step_fused, replayed as a graph of {args.graph} steps"
+                         if args.graph else "rswa_decode_step_fused"),
                    "attention": "standard sliding window (baseline)" if args.attention == "swa"
                    else ("R-SWA" if w.window < steps + max(w.starts()) else
                          "growing full cache (W >= generated tokens)")},

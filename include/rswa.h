@@ -182,6 +182,24 @@ int rswa_decode_step_fused(rswa_cache *c, int32_t layer, const void *q, const vo
  * every layer in this step. */
 int rswa_advance(rswa_cache *c, void *stream);
 
+/* Graph replay of whole decode steps, for callers that capture the
+ * per-step calls to cut launch latency (page section 三 names a faster
+ * ring implementation as open work).  The decode, ring-write and advance
+ * kernels read and advance each request's generated count in device
+ * memory, so a captured graph of k whole steps (every layer's
+ * rswa_ring_write + rswa_decode_step or rswa_decode_step_fused, then
+ * rswa_advance) replays correctly on its own; only the host view that the
+ * calls validate against has to be told.  The calls made while capturing
+ * count as enqueuing those k steps once (they advance the host view);
+ * before each further replay call rswa_note_steps(c, k): it checks that
+ * no step is half done (RSWA_E_STATE) and that every active request stays
+ * below max_positions for k more steps (RSWA_E_POSITION), then advances
+ * the host view by k.  Capture only whole steps of one batch, with kernel
+ * timing off; rswa_set_batch, rswa_prefill and rswa_get_state must not be
+ * captured.  The graph reads the same input and output buffers on every
+ * replay; refill them between replays. */
+int rswa_note_steps(rswa_cache *c, int32_t steps);
+
 /* Read the device-side state of n registered requests (host arrays of n).
  * ring_pos = t mod W (slot offset the next step writes), cache_len =
  * P + min(t, W) (valid entries now), next_pos = P + t.  Any output pointer

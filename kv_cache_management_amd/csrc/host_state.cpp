@@ -406,4 +406,20 @@ void HostState::commit_advance() {
   std::fill(decoded_.begin(), decoded_.end(), 0);
 }
 
+int HostState::check_note_steps(int32_t steps, std::string *err) const {
+  if (steps < 0) return fail(err, RSWA_E_ARG, "steps must be >= 0");
+  if (batch_.empty()) return fail(err, RSWA_E_STATE, "no active batch (rswa_set_batch)");
+  if (step_open()) return fail(err, RSWA_E_STATE, "a decode step is half done");
+  for (int32_t id : batch_) {
+    const RequestState &r = req_[id];
+    if ((int64_t)r.plen + r.t + steps > cfg_.max_positions)
+      return fail(err, RSWA_E_POSITION, "request " + S(id) + " would pass max_positions");
+  }
+  return RSWA_OK;
+}
+
+void HostState::commit_note_steps(int32_t steps) {
+  for (int32_t id : batch_) req_[id].t += steps;
+}
+
 }  // namespace rswa

@@ -160,6 +160,10 @@ class HostState {
   void commit_fused(int32_t layer);
   int check_advance(std::string *err) const;
   void commit_advance();
+  // `steps` whole decode steps of the current batch ran outside the
+  // library's calls (a replayed graph of them).
+  int check_note_steps(int32_t steps, std::string *err) const;
+  void commit_note_steps(int32_t steps);
 
   const RequestState &request(int32_t id) const { return req_[id]; }
   const std::vector<int32_t> &batch() const { return batch_; }

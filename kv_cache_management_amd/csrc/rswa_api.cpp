@@ -466,6 +466,17 @@ int rswa_advance(rswa_cache *c, void *stream) {
   });
 }
 
+int rswa_note_steps(rswa_cache *c, int32_t steps) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    std::string err;
+    int rc = c->st.check_note_steps(steps, &err);
+    if (rc != RSWA_OK) return c->fail(rc, err);
+    c->st.commit_note_steps(steps);
+    return RSWA_OK;
+  });
+}
+
 int rswa_get_state(rswa_cache *c, int32_t n, const int32_t *req_ids, int32_t *ring_pos,
                    int32_t *cache_len, int32_t *next_pos, void *stream) {
   if (!c) return set_global_error(RSWA_E_ARG, "null handle");

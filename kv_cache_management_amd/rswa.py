@@ -37,7 +37,7 @@ EXPORTED = (
     "rswa_prefill", "rswa_set_batch", "rswa_ring_write", "rswa_decode_step",
     "rswa_advance", "rswa_get_state", "rswa_decode_plan", "rswa_status_string",
     "rswa_last_error", "rswa_profile_enable", "rswa_profile_read", "rswa_decode_step_fused",
-    "rswa_measure_read", "rswa_ngram_ban",
+    "rswa_measure_read", "rswa_ngram_ban", "rswa_note_steps",
 )
 RSWA_NGRAM_MAX_WINDOW = 4096
 RSWA_MEASURE_SINK_WORDS = 4096
@@ -126,6 +126,7 @@ def load():
         "rswa_profile_read": (ctypes.c_int, [P, I32, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(ctypes.c_int64), P]),
         "rswa_measure_read": (ctypes.c_int, [P, ctypes.c_uint64, P, P]),
+        "rswa_note_steps": (ctypes.c_int, [P, I32]),
         "rswa_ngram_ban": (ctypes.c_int, [P, ctypes.c_int64, P, I32, I32, I32, P, ctypes.c_int64,
                                           I32, P]),
     }
@@ -392,6 +393,11 @@ class RSWACache:
 
     def advance(self):
         self._check(rswa_advance(self.handle, self.stream()))
+
+    def note_steps(self, steps: int):
+        """Before replaying (again) a captured graph of `steps` whole decode
+        steps: advance the library's host view of the batch."""
+        self._check(load().rswa_note_steps(self.handle, int(steps)))
 
     def get_state(self, req_ids: Sequence[int]):
         st, rp, cl, npos = rswa_get_state(self.handle, req_ids, self.stream())

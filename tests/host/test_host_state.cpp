@@ -275,6 +275,21 @@ static void test_fused_step() {
   CHECK(st.check_advance(&err) == RSWA_OK);
   st.commit_advance();
   CHECK(st.request(1).t == 1);
+  // graph replay bookkeeping: whole steps only, positions checked
+  CHECK(st.check_note_steps(3, &err) == RSWA_OK);
+  st.commit_note_steps(3);
+  CHECK(st.request(1).t == 4);
+  CHECK(st.check_note_steps(-1, &err) == RSWA_E_ARG);
+  CHECK(st.check_ring_write(0, &err) == RSWA_OK);
+  st.commit_ring_write(0);
+  CHECK(st.check_note_steps(1, &err) == RSWA_E_STATE);  // step half done
+  st.commit_decode(0);
+  st.commit_fused(1);
+  st.commit_advance();
+  CHECK(st.request(1).t == 5);
+  const int32_t room = st.config().max_positions - (7 + 5);
+  CHECK(st.check_note_steps(room, &err) == RSWA_OK);
+  CHECK(st.check_note_steps(room + 1, &err) == RSWA_E_POSITION);
 }
 
 static void test_decode_plan() {

@@ -108,6 +108,7 @@ def test_null_handle_calls(R):
     assert R.rswa_ring_write(None, 0, 1, 1, 0) == R.RSWA_E_ARG
     assert R.rswa_decode_step(None, 0, 1, 1, 0) == R.RSWA_E_ARG
     assert R.rswa_advance(None, 0) == R.RSWA_E_ARG
+    assert R.load().rswa_note_steps(None, 1) == R.RSWA_E_ARG
     assert R.rswa_cache_destroy(None) == R.RSWA_OK
 
 
