@@ -4,7 +4,7 @@
 // "开源5天Star破万之后：百度Unlimited-OCR的爆火路径复盘", www.gtnt.cn/news/146005,
 // section 2.1); the page's eager path computes it with a full-matrix softmax
 // (section 三).  Here it is a flash-attention forward: one block per (query
-// tile of 128 rows, head, request), 4 wavefronts of 32 query rows each, key
+// tile of kBM rows, head, request), kWaves wavefronts of 32 query rows each, key
 // tiles of 64 streamed through LDS (K and V tiles double-buffered apart, one
 // barrier per tile), online softmax in base 2.  The loop is software-
 // pipelined one tile deep: while the probabilities of tile k run on the
@@ -57,15 +57,20 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16 *p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-constexpr int kBM = 128;  // query rows per block
-constexpr int kBN = 64;   // keys per tile
-
-#ifndef RSWA_PREFILL_MIN_BLOCKS
-#define RSWA_PREFILL_MIN_BLOCKS 2
+// Wavefronts per block, 32 query rows each.
+#ifndef RSWA_PREFILL_WAVES
+#define RSWA_PREFILL_WAVES 8
 #endif
+constexpr int kWaves = RSWA_PREFILL_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per block
+constexpr int kBN = 64;           // keys per tile
+
+// Blocks per CU the register budget is sized for: two wavefronts per SIMD.
+constexpr int kMinBlocks = 8 / kWaves;
 
 template <int D, bool PAGED>
-__global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   // LDS row strides (elements), chosen for conflict-free reads: K rows are
   // read 16 per 128-bit pass (stride = 4 dwords mod 64 banks); V rows are
@@ -74,8 +79,8 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
   constexpr int VP = D + 32;
   constexpr int DB = D / 32;       // 32-dim blocks of the output
   constexpr int CPR = D / 8;       // 16-byte chunks per key row
-  constexpr int KLD = kBN * CPR / 256;        // 16-byte chunks per thread per tile
-  static_assert(KLD >= 1 && kBN * CPR % 256 == 0, "tile must split evenly");
+  constexpr int KLD = kBN * CPR / kThreads;   // 16-byte chunks per thread per tile
+  static_assert(KLD >= 1 && kBN * CPR % kThreads == 0, "tile must split evenly");
   __shared__ __attribute__((aligned(16))) bf16 lk[2][kBN * KP];
   __shared__ __attribute__((aligned(16))) bf16 lv[2][kBN * VP];
 
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
       for (int it = 0; it < KLD; ++it) {
         // Clamped index: an unconditional load keeps the loop body one
         // basic block.
-        const int j = k0 + (tid + 256 * it) / CPR;
+        const int j = k0 + (tid + kThreads * it) / CPR;
         const int32_t row = table[base + min(j, kend - 1)];
         rows[it] = j < kend ? row : -1;
       }
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
     if constexpr (PAGED)
       return rows[it] >= 0 ? (uint32_t)rows[it] * row_bytes + col_off : a.layer_bytes;
     else
-      return (uint32_t)(k0 + (tid + 256 * it) / CPR) * row_bytes + col_off;
+      return (uint32_t)(k0 + (tid + kThreads * it) / CPR) * row_bytes + col_off;
   };
   auto load_k = [&](int k0, const int32_t *rows) {
 #pragma unroll
@@ -181,14 +186,14 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
   auto store_k = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < KLD; ++it) {
-      const int idx = tid + 256 * it;
+      const int idx = tid + kThreads * it;
       *(uint4 *)(lk[buf] + (idx / CPR) * KP + (idx % CPR) * 8) = kreg[it];
     }
   };
   auto store_v = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < KLD; ++it) {
-      const int idx = tid + 256 * it;
+      const int idx = tid + kThreads * it;
       *(uint4 *)(lv[buf] + (idx / CPR) * VP + (idx % CPR) * 8) = vreg[it];
     }
   };
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(256, RSWA_PREFILL_MIN_BLOCKS) void prefill_mfma_ker
   // Steady state (pairs of steps): tiles k and k + 1 lie wholly below the
   // block's first query row (no mask, every wave takes part) and tile k + 2
   // exists.  The two steps of a pair swap the score registers.
-  const int steady = max(0, min(ntile - 2, 2 * qt - 1)) & ~1;
+  const int steady = max(0, min(ntile - 2, (kBM / kBN) * qt - 1)) & ~1;
   int kt = 0;
   for (; kt < steady; kt += 2) {
     tile_step(std::true_type{}, kt, sA, sB, mxA, mxB);
@@ -384,13 +389,13 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, int head_dim, hipStream_t s
   const dim3 grid((unsigned)a.num_tiles);
   const bool paged = a.pool.table != nullptr;
   if (head_dim == 128 && paged)
-    hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
   else if (head_dim == 64 && paged)
-    hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
