@@ -145,6 +145,41 @@ int rswa_prefill(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids
                  const void *q, const void *k, const void *v, void *out,
                  void *stream);
 
+/* Prefill by chunks: the same as rswa_prefill for rows chunk_start[i] ..
+ * chunk_start[i] + chunk_len[i] - 1 of each request's prefill (host arrays
+ * of n), so a long prompt can be fed in pieces between decode steps of
+ * other requests [section 三 of the page names multi-request memory
+ * scheduling as open work].  q, k, v, out are packed over the chunks
+ * ([sum chunk_len][H][D] in req_ids order).  The chunk's keys/values go to
+ * logical slots chunk_start .. ; its queries are rotated at those positions
+ * and attend causally to every prefill key written so far in this layer
+ * plus their own chunk.  Layer 0 with chunk_start 0 registers the request
+ * (prefill_len, slot_base, zero generated tokens); every other chunk must
+ * repeat those values, start where its layer stopped, and (for layer > 0)
+ * end at or before the rows layer - 1 already holds.  A request joins a
+ * decode batch once every layer holds all its prefill_len rows.
+ * Errors: as rswa_prefill, and RSWA_E_ARG for a chunk outside prefill_len,
+ * RSWA_E_STATE for a chunk out of order. */
+int rswa_prefill_chunk(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids,
+                       const int32_t *prefill_len, const int64_t *slot_base,
+                       const int32_t *chunk_start, const int32_t *chunk_len, const void *q,
+                       const void *k, const void *v, void *out, void *stream);
+
+/* Admission and retirement of requests over the pool's rows (host only, no
+ * device work).  rswa_admit reserves prefill_len + W consecutive rows of the
+ * pool (or slot-table) index space, first fit, for request req_id, which
+ * must be neither registered nor admitted, and returns their first index in
+ * *slot_base; that request's prefill calls must then pass this slot_base.
+ * RSWA_E_CAPACITY when no free range is long enough.  rswa_retire
+ * unregisters n requests (host array; none may be in the active decode
+ * batch, RSWA_E_STATE) and returns their reserved rows, merged with free
+ * neighbours; their ids can be prefilled or admitted again.  Requests
+ * placed by the caller's own slot_base are only unregistered.
+ * rswa_free_rows reports the rows not reserved by rswa_admit. */
+int rswa_admit(rswa_cache *c, int32_t req_id, int32_t prefill_len, int64_t *slot_base);
+int rswa_retire(rswa_cache *c, int32_t n, const int32_t *req_ids);
+int rswa_free_rows(const rswa_cache *c, int64_t *rows);
+
 /* Select the active decode batch (host array of n distinct ids, each
  * prefilled in every layer).  Plans the split-KV work for it.  Must not be
  * called in the middle of a step (after a ring write, before advance). */

@@ -1,6 +1,8 @@
 // Host-side model of an R-SWA handle (see host_state.hpp).  No HIP here.
 #include "host_state.hpp"
 
+#include <iterator>
+
 #include <algorithm>
 #include <cmath>
 #include <numeric>
@@ -103,7 +105,9 @@ PrefillBlob PrefillBlob::make(int n, int64_t t) {
   PrefillBlob b;
   b.req = 0;
   b.plen = align_up(sizeof(int32_t) * n, 16);
-  b.cu = b.plen + align_up(sizeof(int32_t) * n, 16);
+  b.qoff = b.plen + align_up(sizeof(int32_t) * n, 16);
+  b.ptot = b.qoff + align_up(sizeof(int32_t) * n, 16);
+  b.cu = b.ptot + align_up(sizeof(int32_t) * n, 16);
   b.base = b.cu + align_up(sizeof(int64_t) * (n + 1), 16);
   b.tiles = b.base + align_up(sizeof(int64_t) * n, 16);
   b.bytes = b.tiles + align_up(sizeof(int32_t) * 2 * (size_t)t, 16);
@@ -139,9 +143,21 @@ Layout make_layout(const Config &c) {
 HostState::HostState(const Config &c)
     : cfg_(c),
       req_(c.max_requests),
+      done_((size_t)c.max_requests * c.num_layers, 0),
+      admitted_(c.max_requests, {0, 0}),
       in_batch_(c.max_requests, 0),
       written_(c.num_layers, 0),
-      decoded_(c.num_layers, 0) {}
+      decoded_(c.num_layers, 0) {
+  free_[0] = c.row_capacity();
+}
+
+bool HostState::fully_prefilled(int32_t id) const {
+  const RequestState &r = req_[id];
+  if (r.plen < 0) return false;
+  for (int l = 0; l < cfg_.num_layers; ++l)
+    if (prefilled(id, l) != r.plen) return false;
+  return true;
+}
 
 bool HostState::step_open() const {
   for (int l = 0; l < cfg_.num_layers; ++l)
@@ -150,11 +166,13 @@ bool HostState::step_open() const {
 }
 
 int HostState::check_prefill(int32_t layer, int32_t n, const int32_t *ids, const int32_t *plen,
-                             const int64_t *base, std::string *err) const {
+                             const int64_t *base, std::string *err, const int32_t *start,
+                             const int32_t *len) const {
   if (layer < 0 || layer >= cfg_.num_layers)
     return fail(err, RSWA_E_ARG, "layer " + S(layer) + " out of range");
   if (n < 0 || n > cfg_.max_requests) return fail(err, RSWA_E_ARG, "n out of range");
   if (n > 0 && (!ids || !plen || !base)) return fail(err, RSWA_E_ARG, "null host array");
+  if ((start == nullptr) != (len == nullptr)) return fail(err, RSWA_E_ARG, "chunk_start / chunk_len: both or neither");
   std::vector<uint8_t> seen(cfg_.max_requests, 0);
   int64_t total = 0;
   for (int i = 0; i < n; ++i) {
@@ -172,18 +190,29 @@ int HostState::check_prefill(int32_t layer, int32_t n, const int32_t *ids, const
                                             S(base[i] + plen[i] + cfg_.window) + " but the " +
                                             (cfg_.has_table ? "slot table" : "pool") + " has " +
                                             S(cfg_.row_capacity()));
-    total += plen[i];
+    const int32_t s0 = start ? start[i] : 0;
+    const int32_t ln = len ? len[i] : plen[i];
+    if (s0 < 0 || ln < 0 || (int64_t)s0 + ln > plen[i])
+      return fail(err, RSWA_E_ARG, "request " + S(id) + ": chunk " + S(s0) + " + " + S(ln) +
+                                       " outside prefill_len " + S(plen[i]));
+    total += ln;
     if (in_batch_[id])
       return fail(err, RSWA_E_STATE, "request " + S(id) + " is in the active decode batch");
+    const std::pair<int64_t, int64_t> &adm = admitted_[id];
+    if (adm.second && (base[i] != adm.first || (int64_t)plen[i] + cfg_.window > adm.second))
+      return fail(err, RSWA_E_ARG, "request " + S(id) + " was admitted with rows " + S(adm.first) +
+                                       " .. " + S(adm.first + adm.second - 1));
     const RequestState &r = req_[id];
-    if (layer > 0) {
-      if (r.plen < 0) return fail(err, RSWA_E_STATE, "request " + S(id) + " not registered at layer 0");
-      if (r.plen != plen[i] || r.base != base[i])
-        return fail(err, RSWA_E_STATE, "request " + S(id) + " prefill_len/slot_base differ from layer 0");
-      if (r.layers != layer)
-        return fail(err, RSWA_E_STATE, "request " + S(id) + " prefilled through layer " +
-                                           S(r.layers - 1) + "; layers must go in order");
-    }
+    if (layer == 0 && s0 == 0) continue;  // (re)registers the request
+    if (r.plen < 0) return fail(err, RSWA_E_STATE, "request " + S(id) + " not registered (layer 0, chunk at 0)");
+    if (r.plen != plen[i] || r.base != base[i])
+      return fail(err, RSWA_E_STATE, "request " + S(id) + " prefill_len/slot_base differ from its registration");
+    if (prefilled(id, layer) != s0)
+      return fail(err, RSWA_E_STATE, "request " + S(id) + " layer " + S(layer) + " holds " +
+                                         S(prefilled(id, layer)) + " prefill rows, chunk starts at " + S(s0));
+    if (layer > 0 && prefilled(id, layer - 1) < s0 + ln)
+      return fail(err, RSWA_E_STATE, "request " + S(id) + ": layer " + S(layer - 1) + " holds " +
+                                         S(prefilled(id, layer - 1)) + " rows; layers must go in order");
   }
   if (total > cfg_.max_prefill_tokens)
     return fail(err, RSWA_E_CAPACITY, "prefill tokens " + S(total) + " exceed max_prefill_tokens");
@@ -191,21 +220,25 @@ int HostState::check_prefill(int32_t layer, int32_t n, const int32_t *ids, const
 }
 
 void HostState::commit_prefill(int32_t layer, int32_t n, const int32_t *ids, const int32_t *plen,
-                               const int64_t *base) {
+                               const int64_t *base, const int32_t *start, const int32_t *len) {
   for (int i = 0; i < n; ++i) {
-    RequestState &r = req_[ids[i]];
-    if (layer == 0) {
+    const int32_t id = ids[i];
+    RequestState &r = req_[id];
+    const int32_t s0 = start ? start[i] : 0;
+    const int32_t ln = len ? len[i] : plen[i];
+    if (layer == 0 && s0 == 0) {
       r.plen = plen[i];
       r.base = base[i];
       r.t = 0;
-      r.layers = 1;
-    } else {
-      r.layers = layer + 1;
+      std::fill(done_.begin() + (size_t)id * cfg_.num_layers,
+                done_.begin() + (size_t)(id + 1) * cfg_.num_layers, 0);
     }
+    done_[(size_t)id * cfg_.num_layers + layer] = s0 + ln;
   }
 }
 
-PrefillPlan HostState::plan_prefill(int32_t n, const int32_t *plen, int32_t tile) const {
+PrefillPlan HostState::plan_prefill(int32_t n, const int32_t *plen, int32_t tile,
+                                    const int32_t *qoff) const {
   PrefillPlan p;
   p.tile = tile;
   p.cu.assign(n + 1, 0);
@@ -215,14 +248,18 @@ PrefillPlan HostState::plan_prefill(int32_t n, const int32_t *plen, int32_t tile
   }
   p.total_tokens = p.cu[n];
   const int heads = cfg_.num_heads;
-  struct Item { int32_t b, qt, h; };
+  // Work of query tile qt of request b, in key tiles: the rows before the
+  // chunk (qoff / tile) plus the causal part.
+  struct Item { int32_t b, qt, h; int64_t work; };
   struct Group { int32_t b, h, tiles; int64_t work; };
+  auto lead = [&](int b) -> int64_t { return qoff ? qoff[b] / tile : 0; };
   std::vector<Group> groups;
   int64_t n_items = 0;
   for (int b = 0; b < n; ++b) {
     const int32_t nt = (int32_t)ceil_div(plen[b], tile);
     if (nt == 0) continue;
-    for (int h = 0; h < heads; ++h) groups.push_back({b, h, nt, (int64_t)nt * (nt + 1) / 2});
+    const int64_t work = (int64_t)nt * (nt + 1) / 2 + (int64_t)nt * lead(b);
+    for (int h = 0; h < heads; ++h) groups.push_back({b, h, nt, work});
     n_items += (int64_t)nt * heads;
   }
   // Longest-processing-time assignment to XCDs, by whole (request, head)
@@ -238,7 +275,7 @@ PrefillPlan HostState::plan_prefill(int32_t n, const int32_t *plen, int32_t tile
   if (affinity) {
     for (const Group &g : groups) {
       const int x = least();
-      for (int32_t qt = g.tiles - 1; qt >= 0; --qt) xcd[x].push_back({g.b, qt, g.h});
+      for (int32_t qt = g.tiles - 1; qt >= 0; --qt) xcd[x].push_back({g.b, qt, g.h, 0});
       load[x] += g.work;
     }
     size_t longest = 0;
@@ -253,13 +290,13 @@ PrefillPlan HostState::plan_prefill(int32_t n, const int32_t *plen, int32_t tile
     std::vector<Item> items;
     items.reserve(n_items);
     for (const Group &g : groups)
-      for (int32_t qt = 0; qt < g.tiles; ++qt) items.push_back({g.b, qt, g.h});
+      for (int32_t qt = 0; qt < g.tiles; ++qt) items.push_back({g.b, qt, g.h, qt + 1 + lead(g.b)});
     std::stable_sort(items.begin(), items.end(),
-                     [](const Item &x, const Item &y) { return x.qt > y.qt; });
+                     [](const Item &x, const Item &y) { return x.work > y.work; });
     for (const Item &it : items) {
       const int x = least();
       xcd[x].push_back(it);
-      load[x] += it.qt + 1;
+      load[x] += it.work;
     }
   }
   size_t longest = 0;
@@ -293,8 +330,7 @@ int HostState::check_set_batch(int32_t n, const int32_t *ids, std::string *err) 
       return fail(err, RSWA_E_ARG, "request id " + S(id) + " out of range");
     if (seen[id]) return fail(err, RSWA_E_ARG, "request id " + S(id) + " repeated");
     seen[id] = 1;
-    const RequestState &r = req_[id];
-    if (r.plen < 0 || r.layers != cfg_.num_layers)
+    if (!fully_prefilled(id))
       return fail(err, RSWA_E_STATE, "request " + S(id) + " is not prefilled in every layer");
   }
   if (n > 0) {
@@ -420,6 +456,78 @@ int HostState::check_note_steps(int32_t steps, std::string *err) const {
 
 void HostState::commit_note_steps(int32_t steps) {
   for (int32_t id : batch_) req_[id].t += steps;
+}
+
+int HostState::check_admit(int32_t id, int32_t plen, int64_t *base, std::string *err) const {
+  if (id < 0 || id >= cfg_.max_requests) return fail(err, RSWA_E_ARG, "request id out of range");
+  if (plen < 0) return fail(err, RSWA_E_ARG, "negative prefill_len");
+  if (plen > cfg_.max_positions)
+    return fail(err, RSWA_E_POSITION, "prefill_len " + S(plen) + " exceeds max_positions");
+  if (req_[id].plen >= 0 || admitted_[id].second)
+    return fail(err, RSWA_E_STATE, "request " + S(id) + " is registered or admitted (retire it first)");
+  const int64_t need = (int64_t)plen + cfg_.window;
+  for (const auto &f : free_)
+    if (f.second >= need) {
+      *base = f.first;
+      return RSWA_OK;
+    }
+  return fail(err, RSWA_E_CAPACITY, "no " + S(need) + " free consecutive rows (" + S(free_rows()) +
+                                        " free in all)");
+}
+
+void HostState::commit_admit(int32_t id, int32_t plen, int64_t base) {
+  const int64_t need = (int64_t)plen + cfg_.window;
+  auto it = free_.find(base);
+  const int64_t len = it->second;
+  free_.erase(it);
+  if (len > need) free_[base + need] = len - need;
+  admitted_[id] = {base, need};
+}
+
+int HostState::check_retire(int32_t n, const int32_t *ids, std::string *err) const {
+  if (n < 0 || n > cfg_.max_requests) return fail(err, RSWA_E_ARG, "n out of range");
+  if (n > 0 && !ids) return fail(err, RSWA_E_ARG, "null req_ids");
+  std::vector<uint8_t> seen(cfg_.max_requests, 0);
+  for (int i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= cfg_.max_requests) return fail(err, RSWA_E_ARG, "request id out of range");
+    if (seen[id]) return fail(err, RSWA_E_ARG, "request id " + S(id) + " repeated");
+    seen[id] = 1;
+    if (in_batch_[id]) return fail(err, RSWA_E_STATE, "request " + S(id) + " is in the active decode batch");
+  }
+  return RSWA_OK;
+}
+
+void HostState::commit_retire(int32_t n, const int32_t *ids) {
+  for (int i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    req_[id] = RequestState{};
+    std::fill(done_.begin() + (size_t)id * cfg_.num_layers,
+              done_.begin() + (size_t)(id + 1) * cfg_.num_layers, 0);
+    auto [start, len] = admitted_[id];
+    admitted_[id] = {0, 0};
+    if (!len) continue;
+    // return the range, merging with free neighbours
+    auto next = free_.lower_bound(start);
+    if (next != free_.end() && start + len == next->first) {
+      len += next->second;
+      next = free_.erase(next);
+    }
+    if (next != free_.begin()) {
+      auto prev = std::prev(next);
+      if (prev->first + prev->second == start) {
+        prev->second += len;
+        continue;
+      }
+    }
+    free_[start] = len;
+  }
+}
+
+int64_t HostState::free_rows() const {
+  int64_t total = 0;
+  for (const auto &f : free_) total += f.second;
+  return total;
 }
 
 }  // namespace rswa

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cstddef>
 #include <cstdint>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -87,7 +88,9 @@ struct BatchBlob {   // for n active requests and k split work items
 
 struct PrefillBlob {  // for n requests and t query tiles
   size_t req = 0;        // int32 [n]
-  size_t plen = 0;       // int32 [n]
+  size_t plen = 0;       // int32 [n]      rows of this call (the chunk length)
+  size_t qoff = 0;       // int32 [n]      position of the chunk's first row
+  size_t ptot = 0;       // int32 [n]      the request's whole prefill_len
   size_t cu = 0;         // int64 [n + 1]  packed token offset of request b
   size_t base = 0;       // int64 [n]
   size_t tiles = 0;      // int32 [2t]     launch slots: (b, qt << 16 | head), b < 0 = empty
@@ -97,10 +100,9 @@ struct PrefillBlob {  // for n requests and t query tiles
 };
 
 struct RequestState {
-  int32_t plen = -1;     // -1: never registered
+  int32_t plen = -1;     // -1: not registered
   int64_t base = 0;
   int32_t t = 0;         // generated tokens already cached
-  int32_t layers = 0;    // layers prefilled (in order)
 };
 
 struct DecodePlan {
@@ -134,13 +136,35 @@ class HostState {
   explicit HostState(const Config &c);
   const Config &config() const { return cfg_; }
 
+  // Prefill of rows start[i] .. start[i] + len[i] - 1 of each request's
+  // prefill_len plen[i] (start / len null: the whole prefill).  Layer 0 at
+  // start 0 registers the request (prefill_len, slot_base, t = 0); later
+  // chunks continue where the layer stopped, and layer l needs layer l - 1
+  // to have reached the chunk's end.
   int check_prefill(int32_t layer, int32_t n, const int32_t *ids, const int32_t *plen,
-                    const int64_t *base, std::string *err) const;
+                    const int64_t *base, std::string *err, const int32_t *start = nullptr,
+                    const int32_t *len = nullptr) const;
   void commit_prefill(int32_t layer, int32_t n, const int32_t *ids, const int32_t *plen,
-                      const int64_t *base);
+                      const int64_t *base, const int32_t *start = nullptr,
+                      const int32_t *len = nullptr);
   // Plans the packed offsets and the query tiles (of `tile` rows) of a
-  // checked prefill call.
-  PrefillPlan plan_prefill(int32_t n, const int32_t *plen, int32_t tile) const;
+  // checked prefill call: len[b] rows per request starting at position
+  // qoff[b] (null: 0).
+  PrefillPlan plan_prefill(int32_t n, const int32_t *len, int32_t tile,
+                           const int32_t *qoff = nullptr) const;
+  // Rows of request id's prefill already in the cache at layer l.
+  int32_t prefilled(int32_t id, int32_t layer) const { return done_[(size_t)id * cfg_.num_layers + layer]; }
+  bool fully_prefilled(int32_t id) const;
+
+  // Admission and retirement.  admit reserves P + W consecutive rows of the
+  // pool (or slot-table) index space, first fit, for a request not yet
+  // registered; retire unregisters requests outside the decode batch and
+  // returns their reserved rows.
+  int check_admit(int32_t id, int32_t plen, int64_t *base, std::string *err) const;
+  void commit_admit(int32_t id, int32_t plen, int64_t base);
+  int check_retire(int32_t n, const int32_t *ids, std::string *err) const;
+  void commit_retire(int32_t n, const int32_t *ids);
+  int64_t free_rows() const;
   // First logical slot any decode step of a request with prefill_len p may
   // attend to: 0, or with the standard-window baseline p - W + 1.
   int32_t decode_key0(int32_t p) const {
@@ -179,6 +203,9 @@ class HostState {
  private:
   Config cfg_;
   std::vector<RequestState> req_;
+  std::vector<int32_t> done_;                  // [max_requests][num_layers] rows prefilled
+  std::map<int64_t, int64_t> free_;            // free row ranges: start -> length
+  std::vector<std::pair<int64_t, int64_t>> admitted_;  // per id: (start, length), length 0 = none
   std::vector<uint8_t> in_batch_;
   std::vector<int32_t> batch_;
   DecodePlan plan_;

@@ -63,7 +63,9 @@ struct PrefillArgs {
   PoolArgs pool;
   StateArgs st;
   const int32_t *req;         // [n]
-  const int32_t *plen;        // [n]
+  const int32_t *plen;        // [n] rows of this call (chunk length)
+  const int32_t *qoff;        // [n] position (logical slot) of the chunk's first row
+  const int32_t *ptot;        // [n] the request's whole prefill_len
   const int64_t *cu;          // [n + 1] packed token offsets
   const int64_t *base;        // [n]
   const int32_t *tiles;       // [2 * num_tiles] launch slots (b, qt << 16 | head); b < 0 empty

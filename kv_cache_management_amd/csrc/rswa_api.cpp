@@ -264,70 +264,138 @@ int rswa_cache_destroy(rswa_cache *c) {
   return RSWA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids,
+                 const int32_t *prefill_len, const int64_t *slot_base, const int32_t *chunk_start,
+                 const int32_t *chunk_len, const void *q, const void *k, const void *v, void *out,
+                 void *stream) {
+  std::string err;
+  int rc = c->st.check_prefill(layer, n, req_ids, prefill_len, slot_base, &err, chunk_start, chunk_len);
+  if (rc != RSWA_OK) return c->fail(rc, err);
+  const Config &cf = c->cfg;
+  const int tile = rswa::prefill_tile_rows(cf.dtype, cf.head_dim);
+  std::vector<int32_t> qoff(n, 0), rows(prefill_len, prefill_len + n);
+  if (chunk_start) {
+    qoff.assign(chunk_start, chunk_start + n);
+    rows.assign(chunk_len, chunk_len + n);
+  }
+  rswa::PrefillPlan plan = c->st.plan_prefill(n, rows.data(), tile, qoff.data());
+  if (plan.total_tokens > 0 && (!q || !k || !v || !out))
+    return c->fail(RSWA_E_ARG, "null q/k/v/out with prefill tokens");
+  if (plan.num_tiles() > cf.max_prefill_blocks())
+    return c->fail(RSWA_E_CAPACITY, "too many prefill blocks");
+  hipStream_t s = (hipStream_t)stream;
+
+  rswa::PrefillBlob pb = rswa::PrefillBlob::make(n, plan.num_tiles());
+  std::vector<char> blob(pb.bytes, 0);
+  put(blob, pb.req, req_ids, n);
+  put(blob, pb.plen, rows.data(), n);
+  put(blob, pb.qoff, qoff.data(), n);
+  put(blob, pb.ptot, prefill_len, n);
+  put(blob, pb.cu, plan.cu.data(), n + 1);
+  put(blob, pb.base, slot_base, n);
+  put(blob, pb.tiles, plan.tiles.data(), plan.tiles.size());
+  char *dev = c->ws + c->lay.prefill;
+  hipError_t e = c->upload(dev, blob.data(), pb.bytes, s);
+  if (e != hipSuccess) return c->hip_fail(e, "prefill metadata upload");
+
+  rswa::PrefillArgs a{};
+  a.pool = c->pool();
+  a.pool.table = c->slot_table;
+  a.st = c->state();
+  a.req = (const int32_t *)(dev + pb.req);
+  a.plen = (const int32_t *)(dev + pb.plen);
+  a.qoff = (const int32_t *)(dev + pb.qoff);
+  a.ptot = (const int32_t *)(dev + pb.ptot);
+  a.cu = (const int64_t *)(dev + pb.cu);
+  a.base = (const int64_t *)(dev + pb.base);
+  a.tiles = (const int32_t *)(dev + pb.tiles);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.rope = c->rope();
+  a.qscale = c->qscale;
+  a.layer_bytes = (uint32_t)std::min<int64_t>(
+      cf.num_slots * cf.num_heads * cf.head_dim * cf.elem_bytes(), UINT32_MAX);
+  a.n = n;
+  a.heads = cf.num_heads;
+  a.layer = layer;
+  a.num_tiles = (int32_t)plan.num_tiles();
+  a.tile = tile;
+  a.total_tokens = plan.total_tokens;
+  if (layer == 0) {
+    e = rswa::launch_prefill_register(a, s);
+    if (e != hipSuccess) return c->hip_fail(e, "prefill register launch");
+  }
+  e = rswa::launch_prefill_cache_write(a, cf.dtype, cf.head_dim, s);
+  if (e != hipSuccess) return c->hip_fail(e, "prefill cache write launch");
+  const int pi = c->prof_begin(RSWA_KERNEL_PREFILL_ATTENTION, s);
+  e = rswa::launch_prefill_attention(a, cf.dtype, cf.head_dim, s);
+  c->prof_end(RSWA_KERNEL_PREFILL_ATTENTION, pi, s);
+  if (e != hipSuccess) return c->hip_fail(e, "prefill attention launch");
+  c->st.commit_prefill(layer, n, req_ids, prefill_len, slot_base, chunk_start, chunk_len);
+  return RSWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int rswa_prefill(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids,
                  const int32_t *prefill_len, const int64_t *slot_base, const void *q, const void *k,
                  const void *v, void *out, void *stream) {
   if (!c) return set_global_error(RSWA_E_ARG, "null handle");
   return guarded(c, [&]() -> int {
+    return prefill_impl(c, layer, n, req_ids, prefill_len, slot_base, nullptr, nullptr, q, k, v, out,
+                        stream);
+  });
+}
+
+int rswa_prefill_chunk(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids,
+                       const int32_t *prefill_len, const int64_t *slot_base,
+                       const int32_t *chunk_start, const int32_t *chunk_len, const void *q,
+                       const void *k, const void *v, void *out, void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    if (n > 0 && (!chunk_start || !chunk_len)) return c->fail(RSWA_E_ARG, "null chunk_start / chunk_len");
+    return prefill_impl(c, layer, n, req_ids, prefill_len, slot_base, chunk_start, chunk_len, q, k, v,
+                        out, stream);
+  });
+}
+
+int rswa_admit(rswa_cache *c, int32_t req_id, int32_t prefill_len, int64_t *slot_base) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    if (!slot_base) return c->fail(RSWA_E_ARG, "null slot_base");
     std::string err;
-    int rc = c->st.check_prefill(layer, n, req_ids, prefill_len, slot_base, &err);
+    int64_t base = 0;
+    int rc = c->st.check_admit(req_id, prefill_len, &base, &err);
     if (rc != RSWA_OK) return c->fail(rc, err);
-    const Config &cf = c->cfg;
-    const int tile = rswa::prefill_tile_rows(cf.dtype, cf.head_dim);
-    rswa::PrefillPlan plan = c->st.plan_prefill(n, prefill_len, tile);
-    if (plan.total_tokens > 0 && (!q || !k || !v || !out))
-      return c->fail(RSWA_E_ARG, "null q/k/v/out with prefill tokens");
-    if (plan.num_tiles() > cf.max_prefill_blocks())
-      return c->fail(RSWA_E_CAPACITY, "too many prefill blocks");
-    hipStream_t s = (hipStream_t)stream;
-
-    rswa::PrefillBlob pb = rswa::PrefillBlob::make(n, plan.num_tiles());
-    std::vector<char> blob(pb.bytes, 0);
-    put(blob, pb.req, req_ids, n);
-    put(blob, pb.plen, prefill_len, n);
-    put(blob, pb.cu, plan.cu.data(), n + 1);
-    put(blob, pb.base, slot_base, n);
-    put(blob, pb.tiles, plan.tiles.data(), plan.tiles.size());
-    char *dev = c->ws + c->lay.prefill;
-    hipError_t e = c->upload(dev, blob.data(), pb.bytes, s);
-    if (e != hipSuccess) return c->hip_fail(e, "prefill metadata upload");
-
-    rswa::PrefillArgs a{};
-    a.pool = c->pool();
-    a.pool.table = c->slot_table;
-    a.st = c->state();
-    a.req = (const int32_t *)(dev + pb.req);
-    a.plen = (const int32_t *)(dev + pb.plen);
-    a.cu = (const int64_t *)(dev + pb.cu);
-    a.base = (const int64_t *)(dev + pb.base);
-    a.tiles = (const int32_t *)(dev + pb.tiles);
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.out = out;
-    a.rope = c->rope();
-    a.qscale = c->qscale;
-    a.layer_bytes = (uint32_t)std::min<int64_t>(
-        cf.num_slots * cf.num_heads * cf.head_dim * cf.elem_bytes(), UINT32_MAX);
-    a.n = n;
-    a.heads = cf.num_heads;
-    a.layer = layer;
-    a.num_tiles = (int32_t)plan.num_tiles();
-    a.tile = tile;
-    a.total_tokens = plan.total_tokens;
-    if (layer == 0) {
-      e = rswa::launch_prefill_register(a, s);
-      if (e != hipSuccess) return c->hip_fail(e, "prefill register launch");
-    }
-    e = rswa::launch_prefill_cache_write(a, cf.dtype, cf.head_dim, s);
-    if (e != hipSuccess) return c->hip_fail(e, "prefill cache write launch");
-    const int pi = c->prof_begin(RSWA_KERNEL_PREFILL_ATTENTION, s);
-    e = rswa::launch_prefill_attention(a, cf.dtype, cf.head_dim, s);
-    c->prof_end(RSWA_KERNEL_PREFILL_ATTENTION, pi, s);
-    if (e != hipSuccess) return c->hip_fail(e, "prefill attention launch");
-    c->st.commit_prefill(layer, n, req_ids, prefill_len, slot_base);
+    c->st.commit_admit(req_id, prefill_len, base);
+    *slot_base = base;
     return RSWA_OK;
   });
+}
+
+int rswa_retire(rswa_cache *c, int32_t n, const int32_t *req_ids) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  return guarded(c, [&]() -> int {
+    std::string err;
+    int rc = c->st.check_retire(n, req_ids, &err);
+    if (rc != RSWA_OK) return c->fail(rc, err);
+    c->st.commit_retire(n, req_ids);
+    return RSWA_OK;
+  });
+}
+
+int rswa_free_rows(const rswa_cache *c, int64_t *rows) {
+  if (!c || !rows) return set_global_error(RSWA_E_ARG, "null handle or output");
+  *rows = c->st.free_rows();
+  return RSWA_OK;
 }
 
 int rswa_set_batch(rswa_cache *c, int32_t n, const int32_t *req_ids, void *stream) {

@@ -67,8 +67,9 @@ __global__ __launch_bounds__(256) void advance_kernel(AdvanceArgs a) {
 __global__ __launch_bounds__(256) void prefill_register_kernel(PrefillArgs a) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= a.n) return;
+  if (a.qoff[b] != 0) return;  // a later chunk: the request is registered
   const int r = a.req[b];
-  a.st.plen[r] = a.plen[b];
+  a.st.plen[r] = a.ptot[b];
   a.st.t[r] = 0;
   a.st.base[r] = a.base[b];
 }
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void prefill_cache_write_kernel(PrefillArgs a)
   const int64_t tok = pair / a.heads;
   const int h = (int)(pair % a.heads);
   const int b = find_request(a.cu, a.n, tok);
-  const int j = (int)(tok - a.cu[b]);
+  const int j = a.qoff[b] + (int)(tok - a.cu[b]);  // logical slot = position
   const int64_t row = pool_row(a.pool.table, a.base[b], j);
   const int64_t src = (tok * a.heads + h) * D + c * EPL;
   const int64_t dst = (int64_t)a.layer * a.pool.layer_stride + (row * a.heads + h) * D + c * EPL;
@@ -140,17 +141,19 @@ __global__ __launch_bounds__(64) void prefill_attn_valu_kernel(PrefillArgs a) {
   if (b < 0) return;  // empty launch slot
   const int qt = a.tiles[2 * blockIdx.x + 1] >> 16;
   const int h = a.tiles[2 * blockIdx.x + 1] & 0xffff;
-  const int p_len = a.plen[b];
+  const int c_len = a.plen[b];   // rows of this chunk
+  const int q_off = a.qoff[b];   // position of its first row
   const int64_t base = a.base[b];
   const int64_t cu = a.cu[b];
-  const int i = qt * 64 + threadIdx.x;
-  const bool active = i < p_len;
+  const int li = qt * 64 + threadIdx.x;   // row in the chunk
+  const int i = q_off + li;               // its position
+  const bool active = li < c_len;
   const int64_t layer0 = (int64_t)a.layer * a.pool.layer_stride;
 
   float qh[D];
   float o[D];
   if (active) {
-    const T *qp = (const T *)a.q + ((cu + i) * a.heads + h) * D;
+    const T *qp = (const T *)a.q + ((cu + li) * a.heads + h) * D;
     const float2 *cs = a.rope + (int64_t)i * (D / 2);
     for (int d = 0; d < D / 2; ++d) {
       const float2 c = cs[d];
@@ -162,14 +165,14 @@ __global__ __launch_bounds__(64) void prefill_attn_valu_kernel(PrefillArgs a) {
   }
   for (int d = 0; d < D; ++d) o[d] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const int kend = min(p_len, (qt + 1) * 64);
+  const int kend = q_off + min(c_len, (qt + 1) * 64);
   for (int k0 = 0; k0 < kend; k0 += KT) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < KT * D; idx += 64) {
       const int kk = idx / D;
       const int d = idx % D;
       const int j = k0 + kk;
-      if (j < p_len) {
+      if (j < kend) {
         const int64_t off = layer0 + (pool_row(a.pool.table, base, j) * a.heads + h) * D + d;
         ks[kk][d] = to_f(((const T *)a.pool.k)[off]);
         vs[kk][d] = to_f(((const T *)a.pool.v)[off]);
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(64) void prefill_attn_valu_kernel(PrefillArgs a) {
     }
   }
   if (active) {
-    T *op = (T *)a.out + ((cu + i) * a.heads + h) * D;
+    T *op = (T *)a.out + ((cu + li) * a.heads + h) * D;
     const float inv = 1.f / l_run;
     for (int d = 0; d < D; ++d) op[d] = from_f<T>(o[d] * inv);
   }

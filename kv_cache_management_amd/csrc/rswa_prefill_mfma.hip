@@ -88,15 +88,17 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   if (b < 0) return;  // empty launch slot
   const int qt = a.tiles[2 * blockIdx.x + 1] >> 16;
   const int h = a.tiles[2 * blockIdx.x + 1] & 0xffff;
-  const int p_len = a.plen[b];
+  const int c_len = a.plen[b];   // query rows of this call (a chunk of the prefill)
+  const int q_off = a.qoff[b];   // position of the chunk's first row
   const int64_t base = a.base[b];
   const int64_t cu = a.cu[b];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 5;
-  const int q0 = qt * kBM + w * 32;   // first query row of this wave
-  const int qi = q0 + (lane & 31);    // query row of this lane
+  const int li = qt * kBM + w * 32 + (lane & 31);  // this lane's query row in the chunk
+  const int q0 = q_off + qt * kBM + w * 32;        // position of this wave's first row
+  const int qi = q0 + (lane & 31);                 // position of this lane's row
   const int row_stride = a.heads * D;
   const int32_t *table = a.pool.table;
 
@@ -104,8 +106,8 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   bf16x8 qf[KS];
   {
     float qv[KS][8];
-    const bool qok = qi < p_len;
-    const bf16 *qp = (const bf16 *)a.q + ((cu + (qok ? qi : 0)) * a.heads + h) * D;
+    const bool qok = li < c_len;
+    const bf16 *qp = (const bf16 *)a.q + ((cu + (qok ? li : 0)) * a.heads + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 u = qok ? *(const uint4 *)(qp + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
@@ -134,7 +136,8 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   float l_run = 0.f;
   const float qscale = a.qscale;
 
-  const int kend = min(p_len, qt * kBM + kBM);
+  // Keys 0 .. kend-1 are in the pool: earlier chunks plus this one's rows.
+  const int kend = q_off + min(c_len, qt * kBM + kBM);
   const int ntile = (kend + kBN - 1) / kBN;
 
   // ---- tile loads: global -> registers -> LDS (both row-major) -------------
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   // Steady state (pairs of steps): tiles k and k + 1 lie wholly below the
   // block's first query row (no mask, every wave takes part) and tile k + 2
   // exists.  The two steps of a pair swap the score registers.
-  const int steady = max(0, min(ntile - 2, (kBM / kBN) * qt - 1)) & ~1;
+  const int steady = max(0, min(ntile - 2, (q_off + qt * kBM) / kBN - 1)) & ~1;
   int kt = 0;
   for (; kt < steady; kt += 2) {
     tile_step(std::true_type{}, kt, sA, sB, mxA, mxB);
@@ -360,10 +363,10 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
     if (kt + 1 < ntile) tile_step(std::false_type{}, kt + 1, sB, sA, mxB, mxA);
   }
 
-  if (qi >= p_len) return;
+  if (li >= c_len) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
-  bf16 *op = (bf16 *)a.out + ((cu + qi) * a.heads + h) * D;
+  bf16 *op = (bf16 *)a.out + ((cu + li) * a.heads + h) * D;
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll

@@ -37,7 +37,8 @@ EXPORTED = (
     "rswa_prefill", "rswa_set_batch", "rswa_ring_write", "rswa_decode_step",
     "rswa_advance", "rswa_get_state", "rswa_decode_plan", "rswa_status_string",
     "rswa_last_error", "rswa_profile_enable", "rswa_profile_read", "rswa_decode_step_fused",
-    "rswa_measure_read", "rswa_ngram_ban", "rswa_note_steps",
+    "rswa_measure_read", "rswa_ngram_ban", "rswa_note_steps", "rswa_prefill_chunk",
+    "rswa_admit", "rswa_retire", "rswa_free_rows",
 )
 RSWA_NGRAM_MAX_WINDOW = 4096
 RSWA_MEASURE_SINK_WORDS = 4096
@@ -127,6 +128,11 @@ def load():
                                              ctypes.POINTER(ctypes.c_int64), P]),
         "rswa_measure_read": (ctypes.c_int, [P, ctypes.c_uint64, P, P]),
         "rswa_note_steps": (ctypes.c_int, [P, I32]),
+        "rswa_prefill_chunk": (ctypes.c_int, [P, I32, I32, pI32, pI32, pI64, pI32, pI32, P, P, P, P,
+                                              P]),
+        "rswa_admit": (ctypes.c_int, [P, I32, I32, pI64]),
+        "rswa_retire": (ctypes.c_int, [P, I32, pI32]),
+        "rswa_free_rows": (ctypes.c_int, [P, pI64]),
         "rswa_ngram_ban": (ctypes.c_int, [P, ctypes.c_int64, P, I32, I32, I32, P, ctypes.c_int64,
                                           I32, P]),
     }
@@ -181,6 +187,35 @@ def rswa_prefill(handle, layer: int, req_ids, prefill_len, slot_base, q: int, k:
     pl, ppl = _i32(prefill_len)
     sb, psb = _i64(slot_base)
     return load().rswa_prefill(handle, layer, len(ids), pids, ppl, psb, q, k, v, out, stream)
+
+
+def rswa_prefill_chunk(handle, layer: int, req_ids, prefill_len, slot_base, chunk_start, chunk_len,
+                       q: int, k: int, v: int, out: int, stream: int) -> int:
+    ids, pids = _i32(req_ids)
+    pl, ppl = _i32(prefill_len)
+    sb, psb = _i64(slot_base)
+    cs, pcs = _i32(chunk_start)
+    cl, pcl = _i32(chunk_len)
+    return load().rswa_prefill_chunk(handle, layer, len(ids), pids, ppl, psb, pcs, pcl, q, k, v, out,
+                                     stream)
+
+
+def rswa_admit(handle, req_id: int, prefill_len: int):
+    """Returns (status, slot_base)."""
+    base = ctypes.c_int64()
+    st = load().rswa_admit(handle, req_id, prefill_len, ctypes.byref(base))
+    return st, base.value
+
+
+def rswa_retire(handle, req_ids) -> int:
+    ids, pids = _i32(req_ids)
+    return load().rswa_retire(handle, len(ids), pids)
+
+
+def rswa_free_rows(handle):
+    rows = ctypes.c_int64()
+    st = load().rswa_free_rows(handle, ctypes.byref(rows))
+    return st, rows.value
 
 
 def rswa_set_batch(handle, req_ids, stream: int) -> int:
@@ -371,6 +406,28 @@ class RSWACache:
         self._check(rswa_prefill(self.handle, layer, req_ids, prefill_len, slot_base,
                                  self._ptr(q, shp), self._ptr(k, shp), self._ptr(v, shp),
                                  self._ptr(out, shp), self.stream()))
+
+    def prefill_chunk(self, layer: int, req_ids: Sequence[int], prefill_len: Sequence[int],
+                      slot_base: Sequence[int], chunk_start: Sequence[int], chunk_len: Sequence[int],
+                      q, k, v, out):
+        total = int(np.sum(chunk_len)) if len(chunk_len) else 0
+        shp = (total, self.heads, self.head_dim)
+        self._check(rswa_prefill_chunk(self.handle, layer, req_ids, prefill_len, slot_base, chunk_start,
+                                       chunk_len, self._ptr(q, shp), self._ptr(k, shp),
+                                       self._ptr(v, shp), self._ptr(out, shp), self.stream()))
+
+    def admit(self, req_id: int, prefill_len: int) -> int:
+        st, base = rswa_admit(self.handle, req_id, prefill_len)
+        self._check(st)
+        return base
+
+    def retire(self, req_ids: Sequence[int]):
+        self._check(rswa_retire(self.handle, req_ids))
+
+    def free_rows(self) -> int:
+        st, rows = rswa_free_rows(self.handle)
+        self._check(st)
+        return rows
 
     def set_batch(self, req_ids: Sequence[int]):
         self._check(rswa_set_batch(self.handle, req_ids, self.stream()))

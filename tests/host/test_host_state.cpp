@@ -129,7 +129,8 @@ static void test_prefill_order_and_errors() {
 
   CHECK(st.check_prefill(0, 2, ids, pl, base, &err) == RSWA_OK);
   st.commit_prefill(0, 2, ids, pl, base);
-  CHECK(st.request(0).plen == 100 && st.request(0).layers == 1 && st.request(0).t == 0);
+  CHECK(st.request(0).plen == 100 && st.prefilled(0, 0) == 100 && st.prefilled(0, 1) == 0 &&
+        st.request(0).t == 0);
   int32_t pl2[2] = {101, 0};
   CHECK(st.check_prefill(1, 2, ids, pl2, base, &err) == RSWA_E_STATE);  // P differs
   CHECK(st.check_set_batch(2, ids, &err) == RSWA_E_STATE);              // layer 1 missing
@@ -360,6 +361,88 @@ static void test_decode_plan() {
   CHECK(resolve_config(bad, &out, &err) == RSWA_E_ARG);
 }
 
+// Chunked prefill: order rules per layer and across layers.
+static void test_chunked_prefill() {
+  Config c = resolved(base_cfg());
+  HostState st(c);
+  std::string err;
+  int32_t id[1] = {2};
+  int32_t pl[1] = {100};
+  int64_t base[1] = {0};
+  auto chunk = [&](int layer, int s0, int ln) {
+    int32_t a[1] = {s0}, b[1] = {ln};
+    int rc = st.check_prefill(layer, 1, id, pl, base, &err, a, b);
+    if (rc == RSWA_OK) st.commit_prefill(layer, 1, id, pl, base, a, b);
+    return rc;
+  };
+  CHECK(chunk(0, 10, 20) == RSWA_E_STATE);   // not registered: the first chunk starts at 0
+  CHECK(chunk(0, 0, 101) == RSWA_E_ARG);     // past prefill_len
+  CHECK(chunk(0, 0, 40) == RSWA_OK);
+  CHECK(st.prefilled(2, 0) == 40 && st.request(2).plen == 100);
+  CHECK(chunk(0, 50, 10) == RSWA_E_STATE);   // gap
+  CHECK(chunk(1, 0, 41) == RSWA_E_STATE);    // layer 0 holds only 40 rows
+  CHECK(chunk(1, 0, 40) == RSWA_OK);
+  CHECK(chunk(0, 40, 60) == RSWA_OK);
+  int32_t ids[1] = {2};
+  CHECK(st.check_set_batch(1, ids, &err) == RSWA_E_STATE);  // layer 1 incomplete
+  CHECK(chunk(1, 40, 0) == RSWA_OK);         // empty chunk is fine
+  CHECK(chunk(1, 40, 60) == RSWA_OK);
+  CHECK(st.fully_prefilled(2));
+  CHECK(st.check_set_batch(1, ids, &err) == RSWA_OK);
+  // a new layer-0 chunk at 0 re-registers and clears the other layers
+  CHECK(chunk(0, 0, 30) == RSWA_OK);
+  CHECK(st.prefilled(2, 0) == 30 && st.prefilled(2, 1) == 0 && !st.fully_prefilled(2));
+  // plan of a chunk at offset 4096: tiles over the chunk rows only
+  int32_t len[2] = {300, 64};
+  int32_t off[2] = {4096, 0};
+  PrefillPlan pp = st.plan_prefill(2, len, 128, off);
+  int64_t blocks = 0;
+  for (int64_t i = 0; i < pp.num_tiles(); ++i) blocks += pp.tiles[2 * i] >= 0;
+  CHECK(blocks == (3 + 1) * 10 && pp.total_tokens == 364);
+}
+
+// Admission and retirement: first-fit ranges of P + W rows, merged on release.
+static void test_admission() {
+  Config c = resolved(base_cfg());
+  HostState st(c);
+  std::string err;
+  const int64_t cap = c.row_capacity();
+  CHECK(st.free_rows() == cap);
+  int64_t b5 = -1, b6 = -1, b7 = -1;
+  CHECK(st.check_admit(0, 100, &b5, &err) == RSWA_OK);
+  st.commit_admit(0, 100, b5);
+  CHECK(b5 == 0);
+  CHECK(st.check_admit(1, 50, &b6, &err) == RSWA_OK);
+  st.commit_admit(1, 50, b6);
+  CHECK(b6 == 108);  // W = 8
+  CHECK(st.free_rows() == cap - 108 - 58);
+  CHECK(st.check_admit(0, 10, &b7, &err) == RSWA_E_STATE);   // already admitted
+  CHECK(st.check_admit(2, (int32_t)cap, &b7, &err) == RSWA_E_POSITION);
+  // prefill must use the admitted base
+  int32_t id5[1] = {0};
+  int32_t pl5[1] = {100};
+  int64_t wrong[1] = {8};
+  CHECK(st.check_prefill(0, 1, id5, pl5, wrong, &err) == RSWA_E_ARG);
+  int64_t right[1] = {b5};
+  CHECK(st.check_prefill(0, 1, id5, pl5, right, &err) == RSWA_OK);
+  st.commit_prefill(0, 1, id5, pl5, right);
+  int32_t both[2] = {0, 1};
+  CHECK(st.check_retire(2, both, &err) == RSWA_OK);
+  st.commit_retire(1, id5);
+  CHECK(st.request(0).plen == -1 && st.prefilled(0, 0) == 0);
+  CHECK(st.free_rows() == cap - 58);
+  CHECK(st.check_admit(2, 90, &b7, &err) == RSWA_OK);      // first fit: the freed front
+  st.commit_admit(2, 90, b7);
+  CHECK(b7 == 0);
+  int32_t id67[2] = {1, 2};
+  st.commit_retire(2, id67);
+  CHECK(st.free_rows() == cap);
+  int64_t whole = -1;
+  CHECK(st.check_admit(3, (int32_t)std::min<int64_t>(cap - 8, c.max_positions), &whole, &err) == RSWA_OK);
+  CHECK(whole == 0);  // the ranges merged back into one
+  CHECK(st.check_retire(1, nullptr, &err) == RSWA_E_ARG);
+}
+
 int main() {
   test_config();
   test_layout();
@@ -368,6 +451,8 @@ int main() {
   test_step_machine_and_ring();
   test_fused_step();
   test_decode_plan();
+  test_chunked_prefill();
+  test_admission();
   if (g_fail) {
     std::fprintf(stderr, "%d checks failed\n", g_fail);
     return 1;

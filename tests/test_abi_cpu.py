@@ -139,3 +139,10 @@ def test_ngram_ban_rejects_bad_arguments(R):
     assert call(logits=None) == R.RSWA_E_ARG
     assert call(window=R.RSWA_NGRAM_MAX_WINDOW + 1) == R.RSWA_E_UNSUPPORTED
     assert call(n=0, tokens=None, lengths=None, logits=None) == R.RSWA_OK  # nothing to do
+
+
+def test_chunk_and_admission_null_handle(R):
+    assert R.rswa_prefill_chunk(None, 0, [0], [1], [0], [0], [1], 1, 1, 1, 1, 0) == R.RSWA_E_ARG
+    assert R.rswa_admit(None, 0, 10)[0] == R.RSWA_E_ARG
+    assert R.rswa_retire(None, [0]) == R.RSWA_E_ARG
+    assert R.rswa_free_rows(None)[0] == R.RSWA_E_ARG
