@@ -365,6 +365,120 @@ def ngram_ban_timing(torch, rswa, requests=64, vocab=129280, ngram=35, window=12
             "banned_entries": banned, "bound": "launch latency"}
 
 
+def serve(torch, rswa, args):
+    """Serving loop over the library: requests queue up, are admitted into
+    the pool while rows are free (rswa_admit), prefilled in varlen chunks of
+    at most --chunk tokens per iteration across requests
+    (rswa_prefill_chunk, every layer), decoded together once fully
+    prefilled (rswa_decode_step_fused per layer, rswa_advance) up to
+    --max-batch at a time, and retired after --gen tokens (rswa_retire),
+    which frees their rows for the queue.  Synthetic inputs; the whole loop
+    is bracketed by one event pair.  Prints one JSON line."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    stream = torch.cuda.current_stream(dev)
+    L, H, D, Wn = 12, 10, 128, W.WINDOW
+    rng = np.random.default_rng(0)
+    plens = [int(p) for p in rng.integers(272, 8257, args.requests)]
+    rows = int(args.pool_requests * (np.mean(plens) + Wn))
+    table = np.random.default_rng(1).permutation(rows).astype(np.int32)
+    cache = rswa.RSWACache(L, H, D, Wn, max_requests=args.requests, num_slots=rows,
+                           max_prefill_tokens=args.chunk, slot_table=table,
+                           max_splits=max(16384, 4 * args.requests))
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    pf_in = [torch.randn((3, args.chunk, H, D), device=dev, generator=g).to(torch.bfloat16)
+             for _ in range(L)]
+    pf_out = torch.empty((args.chunk, H, D), device=dev, dtype=torch.bfloat16)
+    dec_in = torch.randn((L, 3, args.max_batch, H, D), device=dev, generator=g).to(torch.bfloat16)
+    dec_out = torch.empty((L, args.max_batch, H, D), device=dev, dtype=torch.bfloat16)
+    queue = list(range(args.requests))
+    base, done_rows, gen = {}, {}, {}
+    admitted, batch = [], []
+    finished = 0
+    it = pf_tokens = dec_tokens = 0
+    peak_rows = 0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    while finished < args.requests:
+        it += 1
+        # admission while rows are free
+        while queue:
+            r = queue[0]
+            st, bs = rswa.rswa_admit(cache.handle, r, plens[r])
+            if st == rswa.RSWA_E_CAPACITY:
+                break
+            cache._check(st)
+            base[r], done_rows[r], gen[r] = bs, 0, 0
+            admitted.append(queue.pop(0))
+        peak_rows = max(peak_rows, rows - cache.free_rows())
+        # one varlen prefill call per layer over the next chunks
+        part, budget = [], args.chunk
+        for r in admitted:
+            if budget == 0:
+                break
+            left = plens[r] - done_rows[r]
+            if left > 0:
+                ln = min(left, budget)
+                part.append((r, done_rows[r], ln))
+                budget -= ln
+        if part:
+            ids = [r for r, _, _ in part]
+            tot = sum(ln for _, _, ln in part)
+            for l in range(L):
+                q, k, v = (x[:tot] for x in pf_in[l])
+                cache.prefill_chunk(l, ids, [plens[r] for r in ids], [base[r] for r in ids],
+                                    [s0 for _, s0, _ in part], [ln for _, _, ln in part],
+                                    q, k, v, pf_out[:tot])
+            for r, s0, ln in part:
+                done_rows[r] = s0 + ln
+            pf_tokens += tot
+        # one decode step for up to max_batch fully prefilled requests
+        ready = [r for r in admitted if done_rows[r] == plens[r]][: args.max_batch]
+        if not part and not ready:
+            raise RuntimeError(f"serving loop stalled at iteration {it}: request {queue[:1]} "
+                               f"does not fit the pool of {rows} rows")
+        if ready:
+            if ready != batch:
+                cache.set_batch(ready)
+                batch = ready
+            n = len(batch)
+            for l in range(L):
+                cache.decode_step_fused(l, dec_in[l, 0, :n], dec_in[l, 1, :n], dec_in[l, 2, :n],
+                                        dec_out[l, :n])
+            cache.advance()
+            dec_tokens += n
+            done = []
+            for r in batch:
+                gen[r] += 1
+                if gen[r] == args.gen:
+                    done.append(r)
+            if done:
+                batch = [r for r in batch if r not in done]
+                cache.set_batch(batch)
+                cache.retire(done)
+                admitted = [r for r in admitted if r not in done]
+                finished += len(done)
+    b.record(stream)
+    b.synchronize()
+    gpu_s = a.elapsed_time(b) / 1e3
+    wall = time.perf_counter() - t0
+    cache.close()
+    return {
+        "metric": "R-SWA serving loop: generated tokens/s with chunked prefill, admission and retirement",
+        "value": round(dec_tokens / gpu_s, 1), "unit": "generated tokens/s", "n_gpus": 1,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "serve_mix", "requests": args.requests, "layers": L, "heads": H,
+                   "head_dim": D, "window": Wn, "prefill_len": "U{272..8256}, seed 0",
+                   "generated_per_request": args.gen, "max_batch": args.max_batch,
+                   "chunk_tokens": args.chunk, "pool_rows": rows, "kv_layout": "page-size-1 slot table"},
+        "iterations": it, "prefill_tokens": pf_tokens, "generated_tokens": dec_tokens,
+        "gpu_seconds": round(gpu_s, 3), "wall_seconds": round(wall, 3),
+        "prefill_tokens_per_s": round(pf_tokens / gpu_s, 1),
+        "peak_reserved_rows": int(peak_rows),
+    }
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -471,6 +585,14 @@ def main():
                     help="no per-step event pairs (no step-time percentiles)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured read / GEMM peaks")
+    ap.add_argument("--serve", action="store_true",
+                    help="serving loop with chunked prefill, admission and retirement (own JSON line)")
+    ap.add_argument("--requests", type=int, default=96)
+    ap.add_argument("--gen", type=int, default=256, help="tokens generated per request (--serve)")
+    ap.add_argument("--max-batch", type=int, default=32)
+    ap.add_argument("--chunk", type=int, default=8192, help="prefill tokens per iteration (--serve)")
+    ap.add_argument("--pool-requests", type=float, default=40.0,
+                    help="pool sized for this many average requests (--serve)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -496,6 +618,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2,
                           "launches": 3}))
+        return
+
+    if args.serve:
+        print(json.dumps(serve(torch, rswa, args)), flush=True)
         return
 
     w = W.ALL[args.workload]
