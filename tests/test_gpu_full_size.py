@@ -54,3 +54,39 @@ def test_ragged_mix_full_size():
     inputs = H.Inputs(w)
     res = H.run_gpu(sc, inputs)
     _check_run(sc, res, inputs)
+
+
+def test_doc100_chunked_prefill_full_size():
+    """The 100-page document (4 x 25728 tokens) prefilled in 4096-token
+    chunks, all four requests in every call: sampled rows of every chunk
+    against the oracle, then sampled decode steps (the chunks left the same
+    cache as one whole prefill)."""
+    import torch
+    from kv_cache_management_amd import rswa as R
+    from kv_cache_management_amd import synth
+    from test_gpu_chunked import _decode_and_check
+
+    w = W.DOC100
+    inputs = H.Inputs(w)
+    n = w.batch
+    cache = R.RSWACache(w.layers, w.heads, w.head_dim, w.window, max_requests=n,
+                        num_slots=w.pool_rows(), dtype=w.dtype, max_positions=w.max_positions,
+                        max_prefill_tokens=4 * 4096)
+    ids = list(range(n))
+    bases = w.slot_bases().tolist()
+    p = w.prefill_lens[0]
+    rng = np.random.default_rng(17)
+    for s0 in range(0, p, 4096):
+        ln = min(4096, p - s0)
+        for l in range(w.layers):
+            blocks = [H.to_torch(np.concatenate([inputs.prefill(l, kind, r)[s0:s0 + ln] for r in ids]),
+                                 w.dtype) for kind in (synth.Q_PREFILL, synth.K_PREFILL, synth.V_PREFILL)]
+            out = torch.empty_like(blocks[0])
+            cache.prefill_chunk(l, ids, list(w.prefill_lens), bases, [s0] * n, [ln] * n, *blocks, out)
+            got = H.to_np(out)
+            for b, r in enumerate(ids):
+                rows = sorted({0, ln - 1, *rng.integers(0, ln, 6).tolist()})
+                _, _, want = H.oracle_prefill(w, inputs, l, r, [s0 + x for x in rows])
+                H.compare(got[b * ln:(b + 1) * ln][rows], want, w.dtype, f"chunk {s0} layer {l} req {r}")
+    _decode_and_check(cache, w, inputs, ids, 3, {r: 0 for r in ids})
+    cache.close()
