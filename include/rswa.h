@@ -197,9 +197,11 @@ int rswa_ring_write(rswa_cache *c, int32_t layer, const void *k_new,
 /* Decode attention for `layer` [section 2.1: attention over the whole cache
  * after the write].  For active request b: out[b] = softmax attention of
  * RoPE(q[b], P + t) over logical slots 0 .. L-1 with L = P + min(t + 1, W):
- * the whole prefill and the newest min(t + 1, W) generated tokens.  Split-KV:
+ * the whole prefill and the newest min(t + 1, W) generated tokens (with
+ * RSWA_ATTENTION_SWA only slots max(0, P + t + 1 - W) .. L-1).  Split-KV:
  * partial (max, sum, vector) per split in the workspace, then a combine.
- * Needs this step's rswa_ring_write(layer) first. */
+ * q, out: device [n][H][D] in batch order.  Needs this step's
+ * rswa_ring_write(layer) first (RSWA_E_STATE otherwise). */
 int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out,
                      void *stream);
 
