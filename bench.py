@@ -495,10 +495,13 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0, attention: str = "rswa")
     from kv_cache_management_amd import synth
     from oracle import rswa_oracle as O
 
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        cores = sum(i.get("num_threads", 0) for i in threadpool_info()
-                    if i.get("user_api") == "blas") or 1
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = sum(i.get("num_threads", 0) for i in info) or 1
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
     except Exception:
         cores = 1
     n = w.batch
@@ -552,6 +555,7 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0, attention: str = "rswa")
                    f"requests {reqs} in layer {layer} ({kv / 1e9:.3f} GB of algorithmic KV reads "
                    f"in {t_dec:.2f} s); prefill: one request, first {p} tokens, layer {layer}"),
         "cpu": cpu_model(),
+        "blas": blas,
         "decode_steps_per_s_per_request_layer": round(steps_done / t_dec, 3),
         "prefill_gflops": round(pf_flops / t_pf / 1e9, 3),
     }
