@@ -6,10 +6,12 @@
 // (section 三).  Here it is a flash-attention forward: one block per (query
 // tile of kBM rows, head, request), kWaves wavefronts of 32 query rows each, key
 // tiles of 64 streamed through LDS (K and V tiles double-buffered apart, one
-// barrier per tile), online softmax in base 2.  The loop is software-
-// pipelined one tile deep: while the probabilities of tile k run on the
-// VALU, the scores of tile k + 1 run on the matrix cores, and P.V of tile k
-// runs beside the row max of tile k + 1.
+// barrier per tile), online softmax in base 2.  Tiles go from the pool to LDS
+// without passing through registers (buffer loads with the LDS destination),
+// into an unpadded layout whose 16-byte chunks are XOR-swizzled per row.  The
+// loop is software-pipelined one tile deep: while the probabilities of tile k
+// run on the VALU, the scores of tile k + 1 run on the matrix cores, and P.V
+// of tile k runs beside the row max of tile k + 1.
 //
 // Per wavefront and key tile:
 //   S^T (64 keys x 32 queries) = K (64 x D) . Q^T (D x 32): A = K rows from
@@ -18,7 +20,7 @@
 //     plus one exchange with lane ^ 32.
 //   O^T (D x 32) += V^T (D x 64) . P^T (64 x 32): B = the probabilities,
 //     straight from the S^T registers (converted to bf16), A = V^T, read
-//     from the row-major V tile with the transposing LDS read
+//     from the V tile with the transposing LDS read
 //     (ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
 //     j mod 4 of the 64-bit rows addressed by lanes 4e + j/4, e = 0..3, so
 //     one read turns a 4-key x 16-dim block into 4 keys per lane).  The key
@@ -69,20 +71,50 @@ constexpr int kBN = 64;           // keys per tile
 // Blocks per CU the register budget is sized for: two wavefronts per SIMD.
 constexpr int kMinBlocks = 8 / kWaves;
 
+// 16-byte chunk position of chunk c in LDS row r: c ^ swz(r).  K rows are
+// read 16 at a time at one chunk index, V rows 8 at a time at 4 chunks by
+// the transposing read; the XOR patterns keep both conflict-free without
+// padding, so a tile is one contiguous block the loads can write directly.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Barrier that also publishes this wave's writes to LDS.  The workgroup
+// fence of __syncthreads does not wait for loads whose destination is LDS,
+// so each wave first waits until its own have landed, and its LDS stores
+// too (vmcnt = lgkmcnt = 0; gfx9 s_waitcnt fields: vmcnt [15:14,3:0],
+// expcnt [6:4], lgkmcnt [11:8]).
+__device__ __forceinline__ void lds_publish_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __syncthreads();
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i writes bytes
+// 16 i .. 16 i + 15 after the wave-uniform address `lds`; completion is
+// counted by vmcnt.  The builtin exists only for the device pass (in the host
+// pass it would drop the kernel's launch stub).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, bf16 *lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
+#endif
+}
+
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
-  // LDS row strides (elements), chosen for conflict-free reads: K rows are
-  // read 16 per 128-bit pass (stride = 4 dwords mod 64 banks); V rows are
-  // read 4 keys at a time by the transposing read (stride = 16 dwords mod 64).
-  constexpr int KP = D + 8;
-  constexpr int VP = D + 32;
-  constexpr int DB = D / 32;       // 32-dim blocks of the output
-  constexpr int CPR = D / 8;       // 16-byte chunks per key row
-  constexpr int KLD = kBN * CPR / kThreads;   // 16-byte chunks per thread per tile
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int KLD = kBN * CPR / kThreads;  // chunks per thread per tile
+  constexpr int TILE = kBN * D;              // elements per tile buffer
   static_assert(KLD >= 1 && kBN * CPR % kThreads == 0, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) bf16 lk[2][kBN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 lv[2][kBN * VP];
+  __shared__ __attribute__((aligned(16))) bf16 lk0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 lk1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 lv0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 lv1[TILE];
 
   const int b = a.tiles[2 * blockIdx.x];
   if (b < 0) return;  // empty launch slot
@@ -101,6 +133,18 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   const int qi = q0 + (lane & 31);                 // position of this lane's row
   const int row_stride = a.heads * D;
   const int32_t *table = a.pool.table;
+
+  // Keys past the end of the pool rows are masked, but their V rows still
+  // enter the P.V product with weight 0: start from finite (zero) tiles.
+  {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < TILE / 8; i += kThreads) {
+      ((uint4 *)lk0)[i] = z;
+      ((uint4 *)lk1)[i] = z;
+      ((uint4 *)lv0)[i] = z;
+      ((uint4 *)lv1)[i] = z;
+    }
+  }
 
   // ---- queries: B operand fragments, rotated at their positions ----------
   bf16x8 qf[KS];
@@ -140,11 +184,13 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   const int kend = q_off + min(c_len, qt * kBM + kBM);
   const int ntile = (kend + kBN - 1) / kBN;
 
-  // ---- tile loads: global -> registers -> LDS (both row-major) -------------
-  // 32-bit buffer offsets: contiguous rows use a resource over this request's
-  // first kend rows (keys past kend read zero); paged rows use a resource over
-  // the layer and an offset past its end for keys past kend.
-  uint4 kreg[KLD], vreg[KLD];
+  // ---- tile loads: pool -> LDS directly (16 bytes per lane) --------------
+  // Thread-chunk idx = tid + kThreads * it of a tile lands at byte 16 * idx
+  // of the tile buffer (row idx / CPR, position idx % CPR) and holds chunk
+  // position ^ swz(row) of that key row.  32-bit buffer offsets: contiguous
+  // rows use a resource over this request's first kend rows (keys past kend
+  // read zero); paged rows use a resource over the layer and an offset past
+  // its end for keys past kend.
   const uint32_t row_bytes = (uint32_t)row_stride * 2u;
   const size_t layer_off = (size_t)a.layer * a.pool.layer_stride * 2;
   __amdgpu_buffer_rsrc_t rk, rv;
@@ -156,9 +202,14 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
     rk = make_rsrc((const char *)a.pool.k + req_off, (uint32_t)kend * row_bytes);
     rv = make_rsrc((const char *)a.pool.v + req_off, (uint32_t)kend * row_bytes);
   }
-  const uint32_t col_off = (uint32_t)(h * D * 2 + (tid % CPR) * 16);
+  uint32_t col_off[KLD];
+#pragma unroll
+  for (int it = 0; it < KLD; ++it) {
+    const int idx = tid + kThreads * it;
+    col_off[it] = (uint32_t)(h * D * 2 + (((idx % CPR) ^ swz<D>(idx / CPR)) * 16));
+  }
   // Paged layout: pool rows of a tile's keys, fetched from the slot table a
-  // tile ahead of the loads that use them (-1 past kend).
+  // step ahead of the loads that use them (-1 past kend).
   int32_t rows_k[KLD], rows_v[KLD];
   auto fetch_rows = [&](int32_t *rows, int k0) {
     if constexpr (PAGED) {
@@ -174,50 +225,40 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   };
   auto tile_off = [&](const int32_t *rows, int k0, int it) -> uint32_t {
     if constexpr (PAGED)
-      return rows[it] >= 0 ? (uint32_t)rows[it] * row_bytes + col_off : a.layer_bytes;
+      return rows[it] >= 0 ? (uint32_t)rows[it] * row_bytes + col_off[it] : a.layer_bytes;
     else
-      return (uint32_t)(k0 + (tid + kThreads * it) / CPR) * row_bytes + col_off;
+      return (uint32_t)(k0 + (tid + kThreads * it) / CPR) * row_bytes + col_off[it];
   };
-  auto load_k = [&](int k0, const int32_t *rows) {
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, bf16 *buf, int k0, const int32_t *rows) {
 #pragma unroll
-    for (int it = 0; it < KLD; ++it) kreg[it] = buf_load16(rk, tile_off(rows, k0, it));
-  };
-  auto load_v = [&](int k0, const int32_t *rows) {
-#pragma unroll
-    for (int it = 0; it < KLD; ++it) vreg[it] = buf_load16(rv, tile_off(rows, k0, it));
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < KLD; ++it) {
-      const int idx = tid + kThreads * it;
-      *(uint4 *)(lk[buf] + (idx / CPR) * KP + (idx % CPR) * 8) = kreg[it];
-    }
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < KLD; ++it) {
-      const int idx = tid + kThreads * it;
-      *(uint4 *)(lv[buf] + (idx / CPR) * VP + (idx % CPR) * 8) = vreg[it];
-    }
+    for (int it = 0; it < KLD; ++it)
+      lds_load16(rs, buf + (w * 64 + kThreads * it) * 8, tile_off(rows, k0, it));
   };
   auto shift_rows = [&]() {
 #pragma unroll
     for (int it = 0; it < KLD; ++it) rows_v[it] = rows_k[it];
   };
-  // Transposing-read address of this lane: in its 16-lane group, lane
-  // 4e + q points at key (4g + e), dims (16 * (group & 1) + 4q) of a 32-dim
-  // block; per MFMA step only a constant offset is added.
+  // Read addresses (bytes inside a tile buffer).  K: the lane reads row
+  // 32 j + (lane & 31), chunk 2 ks + g, at position (g ^ swz(row)) ^ 2 ks.
+  // V (transposing read): rows 4 g + (tp >> 2) + 8 hi + 16 hh + 32 j, chunk
+  // 4 d + 2 ((lane >> 4) & 1) + ((tp & 3) >> 1), 8-byte half tp & 1, at
+  // position (its chunk for d = 0 ^ swz(its row for hi = 0)) ^ (4 d + 2 hi).
+  // Rows are 2 D bytes, so the per-read chunk index enters by XOR on the
+  // low address bits and j, hh go into the instruction offset.
+  const int lrow = lane & 31;
   const int tp = lane & 15;
-  const int vtr = (4 * g + (tp >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (tp & 3);
-
-  // S^T = K . Q^T for the key tile in K buffer `buf`, two 32-key blocks.
-  auto scores = [&](int buf, f32x16 *s) {
+  const int vrow = 4 * g + (tp >> 2);
+  const uint32_t ka0 = (uint32_t)(lrow * D * 2 + ((g ^ swz<D>(lrow)) * 16));
+  const uint32_t va0 = (uint32_t)(vrow * D * 2 + 8 * (tp & 1) +
+                                  (((2 * ((lane >> 4) & 1) + ((tp & 3) >> 1)) ^ swz<D>(vrow)) * 16));
+  // S^T = K . Q^T for the key tile in K buffer `kb`, two 32-key blocks.
+  auto scores = [&](const bf16 *kb, f32x16 *s) {
     const f32x16 zero = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const bf16x8 ka = *(const bf16x8 *)(lk[buf] + (32 * j + (lane & 31)) * KP + 16 * ks + 8 * g);
+        const bf16x8 ka = *(const bf16x8 *)((const char *)kb + (ka0 ^ (32u * ks)) + 64 * j * D);
         s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? zero : s[j], 0, 0, 0);
       }
   };
@@ -273,94 +314,86 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
     lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, lsum, false);
     return pb;
   };
-  // O^T += V^T . P^T over the 16 keys (j, hh) of the V tile in buffer `buf`.
-  auto pv_block = [&](int buf, int j, int hh, bf16x8 pb) {
+  // O^T += V^T . P^T over the 16 keys (j, hh) of the V tile `vb`.
+  auto pv_block = [&](const bf16 *vb, int j, int hh, bf16x8 pb) {
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
-      const bf16 *p0 = lv[buf] + vtr + (32 * j + 16 * hh) * VP + 32 * d;
-      const bf16x4 lo = lds_read_tr4(p0);
-      const bf16x4 hi = lds_read_tr4(p0 + 8 * VP);
+      const char *p0 = (const char *)vb + (32 * j + 16 * hh) * D * 2;
+      const bf16x4 lo = lds_read_tr4((const bf16 *)(p0 + (va0 ^ (64u * d))));
+      const bf16x4 hi = lds_read_tr4((const bf16 *)(p0 + 16 * D + (va0 ^ (64u * d + 32u))));
       o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[d], 0, 0, 0);
     }
   };
 
-  // Pipeline.  K tiles and V tiles are double-buffered separately: K(k) in
-  // lk[k & 1], V(k) in lv[k & 1].  At the top of step k the LDS holds K(k+1)
-  // and V(k); registers hold K(k+2) and V(k+1) (loaded a step earlier) and
-  // the masked scores and row max of tile k.  Step k:
-  //   barrier (every wave is done with step k-1, so K(k) and V(k-1) are free)
-  //   rescale if tile k raises the running max
-  //   scores of tile k+1 on the matrix cores, probabilities of tile k on the
-  //   VALU (interleaved)
-  //   store K(k+2) -> lk[k & 1], V(k+1) -> lv[(k+1) & 1]; load V(k+2), K(k+3)
-  //   P.V of tile k on the matrix cores, row max of tile k+1 on the VALU
-  // A wave takes part in tile k only if k * kBN <= its last query row.
+  // Pipeline.  K(k) lives in lk(k & 1), V(k) in lv(k & 1).  At the top of
+  // step k (after the barrier, whose wait also completes every load the
+  // step before issued) the LDS holds K(k+1) and V(k); the registers hold
+  // the masked scores and row max of tile k.  Step k issues the loads of
+  // K(k+2) into lk[k & 1] and V(k+1) into lv[(k+1) & 1] (both last read in
+  // step k-1), then scores of tile k+1 beside the probabilities of tile k,
+  // then P.V of tile k beside the row max of tile k+1.  A wave takes part
+  // in tile k only if k * kBN <= its last query row.
   const int last_q = q0 + 31;
-  auto tile_step = [&](auto steady_c, int k, f32x16 *sc, f32x16 *sn, float mx_cur, float &mx_nxt) {
+  auto tile_step = [&](auto steady_c, auto par_c, int k, f32x16 *sc, f32x16 *sn, float mx_cur, float &mx_nxt) {
     constexpr bool kSteady = decltype(steady_c)::value;
-    __syncthreads();
+    constexpr int kPar = decltype(par_c)::value;
+    bf16 *kcur = kPar ? lk1 : lk0;   // K(k): free, receives K(k+2)
+    bf16 *knxt = kPar ? lk0 : lk1;   // K(k+1)
+    bf16 *vcur = kPar ? lv1 : lv0;   // V(k)
+    bf16 *vnxt = kPar ? lv0 : lv1;   // free, receives V(k+1)
+    lds_publish_barrier();
+    if (kSteady || k + 2 < ntile) dma(rk, kcur, (k + 2) * kBN, rows_k);
+    if (kSteady || k + 1 < ntile) dma(rv, vnxt, (k + 1) * kBN, rows_v);
+    shift_rows();
+    fetch_rows(rows_k, (k + 3) * kBN);
     const bool act = kSteady || k * kBN <= last_q;
     const bool act_n = kSteady || (k + 1 < ntile && (k + 1) * kBN <= last_q);
     if (act) rescale(mx_cur);
-    if (act_n) scores((k + 1) & 1, sn);
+    if (act_n) scores(knxt, sn);
     float lsum = 0.f;
     bf16x8 p00, p01, p10, p11;
     if (act) {
       p00 = probs(sc, 0, 0, lsum);
       p01 = probs(sc, 0, 1, lsum);
       p10 = probs(sc, 1, 0, lsum);
-    }
-    if (kSteady || k + 2 < ntile) store_k(k & 1);
-    if (kSteady || k + 1 < ntile) store_v((k + 1) & 1);
-    if (kSteady || k + 2 < ntile) load_v((k + 2) * kBN, rows_v);
-    if (kSteady || k + 3 < ntile) load_k((k + 3) * kBN, rows_k);
-    shift_rows();
-    fetch_rows(rows_k, (k + 4) * kBN);
-    if (act) {
-      pv_block(k & 1, 0, 0, p00);
-      pv_block(k & 1, 0, 1, p01);
-      pv_block(k & 1, 1, 0, p10);
+      pv_block(vcur, 0, 0, p00);
+      pv_block(vcur, 0, 1, p01);
+      pv_block(vcur, 1, 0, p10);
       p11 = probs(sc, 1, 1, lsum);
-      pv_block(k & 1, 1, 1, p11);
+      pv_block(vcur, 1, 1, p11);
       l_run += lsum;
     }
     if (act_n) mx_nxt = mask_max(sn, (k + 1) * kBN, !kSteady);
   };
 
-  // Prologue: K(0), V(0), K(1) into LDS; V(1), K(2) loading; rows of tiles
-  // 2 and 3 fetched; scores and row max of tile 0 (every wave takes part).
+  // Prologue: K(0), V(0), K(1) loaded; rows of tiles 1 (V) and 2 (K) fetched.
   f32x16 sA[2], sB[2];
   float mxA = -INFINITY, mxB = -INFINITY;
   fetch_rows(rows_k, 0);
-  load_k(0, rows_k);
-  load_v(0, rows_k);
   fetch_rows(rows_v, kBN);
-  store_k(0);
-  store_v(0);
-  load_k(kBN, rows_v);
-  load_v(kBN, rows_v);
+  lds_publish_barrier();  // zero fill done before any load writes the tiles
+  dma(rk, lk0, 0, rows_k);
+  dma(rv, lv0, 0, rows_k);
+  dma(rk, lk1, kBN, rows_v);
   fetch_rows(rows_k, 2 * kBN);
-  store_k(1);
-  load_k(2 * kBN, rows_k);
-  shift_rows();
-  fetch_rows(rows_k, 3 * kBN);
-  __syncthreads();
-  scores(0, sA);
+  lds_publish_barrier();
+  scores(lk0, sA);
   mxA = mask_max(sA, 0, true);
 
   // Steady state (pairs of steps): tiles k and k + 1 lie wholly below the
   // block's first query row (no mask, every wave takes part) and tile k + 2
-  // exists.  The two steps of a pair swap the score registers.
+  // exists.  The two steps of a pair swap the score registers and buffers.
   const int steady = max(0, min(ntile - 2, (q_off + qt * kBM) / kBN - 1)) & ~1;
   int kt = 0;
   for (; kt < steady; kt += 2) {
-    tile_step(std::true_type{}, kt, sA, sB, mxA, mxB);
-    tile_step(std::true_type{}, kt + 1, sB, sA, mxB, mxA);
+    tile_step(std::true_type{}, std::integral_constant<int, 0>{}, kt, sA, sB, mxA, mxB);
+    tile_step(std::true_type{}, std::integral_constant<int, 1>{}, kt + 1, sB, sA, mxB, mxA);
   }
   for (; kt < ntile; kt += 2) {
-    tile_step(std::false_type{}, kt, sA, sB, mxA, mxB);
-    if (kt + 1 < ntile) tile_step(std::false_type{}, kt + 1, sB, sA, mxB, mxA);
+    tile_step(std::false_type{}, std::integral_constant<int, 0>{}, kt, sA, sB, mxA, mxB);
+    if (kt + 1 < ntile)
+      tile_step(std::false_type{}, std::integral_constant<int, 1>{}, kt + 1, sB, sA, mxB, mxA);
   }
 
   if (li >= c_len) return;
