@@ -378,6 +378,25 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   dma(rk, lk1, kBN, rows_v);
   fetch_rows(rows_k, 2 * kBN);
   lds_publish_barrier();
+
+  // A wave with no valid query row (the tail of a chunk's last query tile)
+  // only takes its share of the loads, behind the same barriers.
+  if (qt * kBM + w * 32 >= c_len) {
+    auto load_step = [&](auto par_c, int k) {
+      constexpr int kPar = decltype(par_c)::value;
+      lds_publish_barrier();
+      if (k + 2 < ntile) dma(rk, kPar ? lk1 : lk0, (k + 2) * kBN, rows_k);
+      if (k + 1 < ntile) dma(rv, kPar ? lv0 : lv1, (k + 1) * kBN, rows_v);
+      shift_rows();
+      fetch_rows(rows_k, (k + 3) * kBN);
+    };
+    for (int kt = 0; kt < ntile; kt += 2) {
+      load_step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < ntile) load_step(std::integral_constant<int, 1>{}, kt + 1);
+    }
+    return;
+  }
+
   scores(lk0, sA);
   mxA = mask_max(sA, 0, true);
 
