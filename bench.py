@@ -295,8 +295,10 @@ def traffic_from_profile(workload: str):
 
 def measured_peaks(torch, rswa, read_gib: int = 4):
     """What this GPU reaches on its own: a streaming read of a 4 GiB buffer
-    with the decode kernel's load instruction (rswa_measure_read), and a
-    large bf16 GEMM through the vendor library (torch.matmul -> hipBLASLt)."""
+    with the decode kernel's load instruction (rswa_measure_read), a large
+    bf16 GEMM through the vendor library (torch.matmul -> hipBLASLt), and the
+    prefill kernel's MFMA alone on random and on zero operands
+    (rswa_measure_mfma)."""
     dev = torch.device("cuda", torch.cuda.current_device())
     stream = torch.cuda.current_stream(dev)
     nbytes = read_gib << 30
@@ -328,10 +330,30 @@ def measured_peaks(torch, rswa, read_gib: int = 4):
     b.synchronize()
     gemm_tflops = 2 * n ** 3 * reps / (a.elapsed_time(b) / 1e3) / 1e12
     del x, y, z
+    # Matrix-core rate with the prefill kernel's MFMA alone, on N(0, 1) bf16
+    # operands and on zeros: the gap is the clock the matrix cores lose to
+    # the power their random operands draw.
+    mfma = {}
+    sink = torch.empty(512, dtype=torch.float32, device=dev)
+    for kind in ("random", "zeros"):
+        ops = (torch.randn if kind == "random" else torch.zeros)(
+            (rswa.RSWA_MEASURE_MFMA_FRAGMENTS, 8), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        st = rswa.rswa_measure_mfma(ops.data_ptr(), 300_000, sink.data_ptr(), stream.cuda_stream)
+        assert st == 0, st
+        iters = 1_500_000
+        a.record(stream)
+        rswa.rswa_measure_mfma(ops.data_ptr(), iters, sink.data_ptr(), stream.cuda_stream)
+        b.record(stream)
+        b.synchronize()
+        mfma[kind] = rswa.RSWA_MEASURE_MFMA_FLOPS_PER_ITER * iters / (a.elapsed_time(b) / 1e3) / 1e12
+        del ops
     torch.cuda.empty_cache()
     return {"hbm_read_GBps": round(read_gbs, 1), "hbm_read": f"rswa_measure_read over {read_gib} GiB",
             "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
-            "bf16_gemm": f"torch.matmul {n}x{n}x{n} bf16"}
+            "bf16_gemm": f"torch.matmul {n}x{n}x{n} bf16",
+            "bf16_mfma_random_TFLOPs": round(mfma["random"], 1),
+            "bf16_mfma_zeros_TFLOPs": round(mfma["zeros"], 1),
+            "bf16_mfma": "rswa_measure_mfma, 32x32x16 bf16 MFMA only, 2 waves/SIMD, ~0.3 s per figure"}
 
 
 def ngram_ban_timing(torch, rswa, requests=64, vocab=129280, ngram=35, window=128, reps=200):
@@ -737,13 +759,15 @@ def main():
     }
     out["ngram_ban"] = ngram_ban_timing(torch, rswa)
     if not args.no_peaks:
-        log("measuring the read and GEMM peaks")
+        log("measuring the read, GEMM and MFMA peaks")
         mp = measured_peaks(torch, rswa)
         out["measured_peak"] = mp
         if roofline:
             roofline["frac_of_measured_read"] = round(roofline["achieved"] / mp["hbm_read_GBps"], 4)
         if prefill_kernel:
             prefill_kernel["frac_of_measured_gemm"] = round(prefill_kernel["achieved"] / mp["bf16_gemm_TFLOPs"], 4)
+            prefill_kernel["frac_of_measured_mfma"] = round(
+                prefill_kernel["achieved"] / mp["bf16_mfma_random_TFLOPs"], 4)
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.attention)

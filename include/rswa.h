@@ -297,6 +297,21 @@ int rswa_ngram_ban(const int32_t *tokens, int64_t token_stride, const int32_t *l
 enum { RSWA_MEASURE_SINK_WORDS = 4096 };
 int rswa_measure_read(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
 
+/* Measurement helper, not part of the attention path: the bf16 matrix-core
+ * rate of this GPU with the prefill kernel's instruction
+ * (v_mfma_f32_32x32x16_bf16).  512 blocks of 256 threads (two wavefronts per
+ * SIMD on 256 CUs); every lane loads two A and two B fragments of 8 bf16
+ * from `operands` (device, RSWA_MEASURE_MFMA_FRAGMENTS x 8 bf16, read only)
+ * and runs `iters` iterations of four independent 32x32x16 products, so one
+ * call does RSWA_MEASURE_MFMA_FLOPS_PER_ITER * iters flops; the rate depends
+ * on the operand values (power), so fill `operands` like the data being
+ * priced.  Writes one float per block to `sink` (device, at least 512).
+ * Asynchronous on `stream`.  Errors: RSWA_E_ARG (null pointer, iters < 1),
+ * RSWA_E_HIP (launch failure). */
+enum { RSWA_MEASURE_MFMA_FRAGMENTS = 65536 };
+#define RSWA_MEASURE_MFMA_FLOPS_PER_ITER (2048.0 * 4.0 * 2.0 * 32.0 * 32.0 * 16.0)
+int rswa_measure_mfma(const void *operands, int32_t iters, float *sink, void *stream);
+
 /* Static name of a status code. */
 const char *rswa_status_string(int status);
 

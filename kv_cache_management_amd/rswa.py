@@ -38,10 +38,12 @@ EXPORTED = (
     "rswa_advance", "rswa_get_state", "rswa_decode_plan", "rswa_status_string",
     "rswa_last_error", "rswa_profile_enable", "rswa_profile_read", "rswa_decode_step_fused",
     "rswa_measure_read", "rswa_ngram_ban", "rswa_note_steps", "rswa_prefill_chunk",
-    "rswa_admit", "rswa_retire", "rswa_free_rows",
+    "rswa_admit", "rswa_retire", "rswa_free_rows", "rswa_measure_mfma",
 )
 RSWA_NGRAM_MAX_WINDOW = 4096
 RSWA_MEASURE_SINK_WORDS = 4096
+RSWA_MEASURE_MFMA_FRAGMENTS = 65536
+RSWA_MEASURE_MFMA_FLOPS_PER_ITER = 2048.0 * 4.0 * 2.0 * 32.0 * 32.0 * 16.0
 RSWA_KERNEL_DECODE_SPLIT = 0
 RSWA_KERNEL_PREFILL_ATTENTION = 1
 
@@ -127,6 +129,7 @@ def load():
         "rswa_profile_read": (ctypes.c_int, [P, I32, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(ctypes.c_int64), P]),
         "rswa_measure_read": (ctypes.c_int, [P, ctypes.c_uint64, P, P]),
+        "rswa_measure_mfma": (ctypes.c_int, [P, I32, P, P]),
         "rswa_note_steps": (ctypes.c_int, [P, I32]),
         "rswa_prefill_chunk": (ctypes.c_int, [P, I32, I32, pI32, pI32, pI64, pI32, pI32, P, P, P, P,
                                               P]),
@@ -274,6 +277,13 @@ def rswa_measure_read(buf: int, nbytes: int, sink: int, stream: int) -> int:
     """Streaming read of nbytes at device address buf (sink: device buffer of
     RSWA_MEASURE_SINK_WORDS uint32)."""
     return load().rswa_measure_read(buf, nbytes, sink, stream)
+
+
+def rswa_measure_mfma(operands: int, iters: int, sink: int, stream: int) -> int:
+    """bf16 matrix-core loop on RSWA_MEASURE_MFMA_FRAGMENTS x 8 bf16 operands at
+    device address operands (sink: device buffer of at least 512 floats);
+    RSWA_MEASURE_MFMA_FLOPS_PER_ITER * iters flops."""
+    return load().rswa_measure_mfma(operands, iters, sink, stream)
 
 
 def rswa_ngram_ban(tokens: int, token_stride: int, lengths: int, n: int, ngram: int, window: int,

@@ -120,6 +120,13 @@ def test_measure_read_rejects_bad_arguments(R):
     assert R.rswa_measure_read(1, 1 << 45, 1, None) == R.RSWA_E_UNSUPPORTED
 
 
+def test_measure_mfma_rejects_bad_arguments(R):
+    """Argument checks run before any launch, so they hold without a GPU."""
+    assert R.rswa_measure_mfma(None, 1, 1, None) == R.RSWA_E_ARG
+    assert R.rswa_measure_mfma(1, 1, None, None) == R.RSWA_E_ARG
+    assert R.rswa_measure_mfma(1, 0, 1, None) == R.RSWA_E_ARG
+
+
 def test_ngram_ban_rejects_bad_arguments(R):
     ok = dict(tokens=1, token_stride=128, lengths=1, n=4, ngram=35, window=128, logits=1,
               vocab=129280, dtype=R.RSWA_DTYPE_BF16, stream=None)

@@ -1,0 +1,44 @@
+"""GPU checks of the measurement helpers (not part of the attention path):
+the MFMA loop computes what it claims (exact sums on operands of ones and
+zeros), and the streaming read launches over a buffer that is not a
+multiple of its chunk size."""
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def _rswa():
+    from kv_cache_management_amd import rswa
+
+    rswa.load()
+    return rswa
+
+
+@pytest.mark.parametrize("value,iters", [(1.0, 3), (0.0, 5), (2.0, 1)])
+def test_measure_mfma_exact_on_constant_operands(value, iters):
+    """Every 32x32x16 product of constant operands v adds 16 v^2 to each of
+    its 16 accumulators per lane; four chains, summed over the 64 lanes of
+    the block's first wave: 65536 v^2 iters, exact in fp32."""
+    import torch
+
+    R = _rswa()
+    ops = torch.full((R.RSWA_MEASURE_MFMA_FRAGMENTS, 8), value, device="cuda", dtype=torch.bfloat16)
+    sink = torch.full((512,), float("nan"), device="cuda", dtype=torch.float32)
+    st = R.rswa_measure_mfma(ops.data_ptr(), iters, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, R.load().rswa_status_string(st)
+    torch.cuda.synchronize()
+    want = 65536.0 * value * value * iters
+    assert torch.all(sink == want), (sink[:4].tolist(), want)
+
+
+def test_measure_read_runs_on_a_ragged_buffer():
+    import torch
+
+    R = _rswa()
+    nbytes = (3 << 20) + 48
+    buf = torch.full((nbytes,), 7, device="cuda", dtype=torch.uint8)
+    sink = torch.empty(R.RSWA_MEASURE_SINK_WORDS, device="cuda", dtype=torch.int32)
+    st = R.rswa_measure_read(buf.data_ptr(), nbytes, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, R.load().rswa_status_string(st)
+    torch.cuda.synchronize()
