@@ -95,12 +95,10 @@ __device__ __forceinline__ void lds_publish_barrier() {
 
 // 16 bytes per lane from a buffer straight into LDS: lane i writes bytes
 // 16 i .. 16 i + 15 after the wave-uniform address `lds`; completion is
-// counted by vmcnt.  The builtin exists only for the device pass (in the host
-// pass it would drop the kernel's launch stub).
+// counted by vmcnt.  (Kept out of the kernel's lambdas: called directly from
+// one, the builtin makes the host pass drop the kernel's launch stub.)
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, bf16 *lds, uint32_t voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
-#endif
 }
 
 template <int D, bool PAGED>
