@@ -87,7 +87,7 @@ hipError_t launch_decode_split(const DecodeArgs &a, int dtype, int head_dim, hip
 hipError_t launch_decode_combine(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
-// bf16 MFMA causal prefill attention (128-row query tiles).
+// bf16 MFMA causal prefill attention (query tiles of prefill_mfma_rows() rows).
 bool prefill_mfma_supported(int dtype, int head_dim);
 // Query rows per block of the MFMA prefill kernel.
 int prefill_mfma_rows();
