@@ -169,6 +169,20 @@ def test_small_ragged_all_variants(dtype, head_dim, paged):
     _check_run(sc, res, inputs)
 
 
+@pytest.mark.parametrize("head_dim,paged", [(128, True), (128, False), (64, True)])
+def test_prefill_at_tile_boundaries(head_dim, paged):
+    """Prefill lengths on and around the bf16 kernel's 64-key tiles and
+    256-row query tiles (no partial tile, one row past, one row short),
+    every prefill row and a few decode steps against the oracle."""
+    w = dataclasses.replace(SMALL_RAGGED, prefill_lens=(255, 256, 257, 511, 512, 513, 768),
+                            start_steps=None, head_dim=head_dim, paged=paged, decode_steps=4,
+                            wid=300 + head_dim + paged)
+    sc = H.Scenario(w, steps=w.decode_steps, check_steps=range(w.decode_steps))
+    inputs = H.Inputs(w)
+    res = H.run_gpu(sc, inputs)
+    _check_run(sc, res, inputs)
+
+
 @pytest.mark.parametrize("split", [64, 128, 1024])
 def test_split_size_does_not_change_results(split):
     w = dataclasses.replace(SMALL_RAGGED, prefill_lens=(700, 129, 1000), start_steps=(0, 20, 3),
