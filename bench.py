@@ -356,6 +356,29 @@ def measured_peaks(torch, rswa, read_gib: int = 4):
             "bf16_mfma": "rswa_measure_mfma, 32x32x16 bf16 MFMA only, 2 waves/SIMD, ~0.3 s per figure"}
 
 
+def prefill_main(runs: int = 3):
+    """Prefill attention kernel on the 100-page document (4 x 25728 tokens,
+    one layer): the configuration whose prefill is the main TFLOP/s
+    datapoint, measured beside any --workload with the same kernel events."""
+    from kv_cache_management_amd import rswa
+
+    w = W.DOC100
+    job = Job(w, 1)
+    job.run(profile_kernels=False)
+    for _ in range(runs):
+        job.run(profile_kernels=True)
+    job.times_ms()
+    ms, cnt = job.kernel_time(rswa.RSWA_KERNEL_PREFILL_ATTENTION)
+    job.cache.close()
+    avg_s = ms / cnt / 1e3
+    per_launch = prefill_flops(w) / w.layers
+    tf = per_launch / avg_s / 1e12
+    return {"workload": w.name, "requests": w.batch, "prefill_len": w.prefill_lens[0],
+            "bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "avg_launch_us": round(avg_s * 1e6, 1), "launches": cnt}
+
+
 def ngram_ban_timing(torch, rswa, requests=64, vocab=129280, ngram=35, window=128, reps=200):
     """Time of one rswa_ngram_ban call at the page's sizes: 64 requests,
     129,280-token vocabulary, n = 35 inside a 128-token window, bf16 logits.
@@ -619,6 +642,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=8192, help="prefill tokens per iteration (--serve)")
     ap.add_argument("--pool-requests", type=float, default=40.0,
                     help="pool sized for this many average requests (--serve)")
+    ap.add_argument("--no-prefill-main", action="store_true",
+                    help="skip the prefill-kernel timing on the 100-page document")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -753,11 +778,17 @@ def main():
         "decode_step_times": step_stats,
         "roofline": roofline,
         "prefill_kernel": prefill_kernel,
+        "prefill_main": None,
         "ngram_ban": None,
         "measured_peak": None,
         "cpu_baseline": None,
     }
     out["ngram_ban"] = ngram_ban_timing(torch, rswa)
+    if prefill_kernel and w.name == W.DOC100.name:
+        out["prefill_main"] = dict(prefill_kernel, workload=w.name)
+    elif not args.no_prefill_main and not args.no_kernel_events:
+        log("timing the prefill kernel on the 100-page document")
+        out["prefill_main"] = prefill_main()
     if not args.no_peaks:
         log("measuring the read, GEMM and MFMA peaks")
         mp = measured_peaks(torch, rswa)
@@ -768,6 +799,9 @@ def main():
             prefill_kernel["frac_of_measured_gemm"] = round(prefill_kernel["achieved"] / mp["bf16_gemm_TFLOPs"], 4)
             prefill_kernel["frac_of_measured_mfma"] = round(
                 prefill_kernel["achieved"] / mp["bf16_mfma_random_TFLOPs"], 4)
+        if out["prefill_main"]:
+            out["prefill_main"]["frac_of_measured_mfma"] = round(
+                out["prefill_main"]["achieved"] / mp["bf16_mfma_random_TFLOPs"], 4)
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.attention)
