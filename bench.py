@@ -226,32 +226,29 @@ class Job:
     def _run_graph(self):
         torch, lib, h = self.torch, self.lib, self.h
         k = self.graph_k
-        first_free = False
-        if self.graph is None:
-            # capture on a side stream; the capture calls count as enqueuing
-            # the first replay's k steps
-            self.graph = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(self.stream)
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(self.graph, stream=side):
-                    sptr = side.cuda_stream
-                    L = self.w.layers
-                    for i in range(k):
-                        g = self.pre + i
-                        for l in range(L):
-                            blk = self.dec_ptr0 + ((g * L + l) * 3) * self.row_bytes
-                            self._check(lib.rswa_decode_step_fused(
-                                h, l, blk, blk + self.row_bytes, blk + 2 * self.row_bytes,
-                                self.out_ptr[l], sptr))
-                        self._check(lib.rswa_advance(h, sptr))
-            self.stream.wait_stream(side)
-            first_free = True
+        # A graph holds the batch plan of its capture, and every job sets the
+        # batch again after its pre-roll: capture afresh on a side stream.
+        # The capture calls count as enqueuing the first replay's k steps.
+        self.graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(self.stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(self.graph, stream=side):
+                sptr = side.cuda_stream
+                L = self.w.layers
+                for i in range(k):
+                    g = self.pre + i
+                    for l in range(L):
+                        blk = self.dec_ptr0 + ((g * L + l) * 3) * self.row_bytes
+                        self._check(lib.rswa_decode_step_fused(
+                            h, l, blk, blk + self.row_bytes, blk + 2 * self.row_bytes,
+                            self.out_ptr[l], sptr))
+                    self._check(lib.rswa_advance(h, sptr))
+        self.stream.wait_stream(side)
         self.ev["d0"].record(self.stream)
         for j in range(self.steps // k):
-            if not first_free:
+            if j > 0:
                 self._check(lib.rswa_note_steps(h, k))
-            first_free = False
             self.graph.replay()
         self.ev["d1"].record(self.stream)
 

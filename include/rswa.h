@@ -181,8 +181,13 @@ int rswa_retire(rswa_cache *c, int32_t n, const int32_t *req_ids);
 int rswa_free_rows(const rswa_cache *c, int64_t *rows);
 
 /* Select the active decode batch (host array of n distinct ids, each
- * prefilled in every layer).  Plans the split-KV work for it.  Must not be
- * called in the middle of a step (after a ring write, before advance). */
+ * prefilled in every layer) [section 2.1: each request decodes over its own
+ * cache -- its whole prefill plus its own W-slot ring -- so a batch is a set
+ * of independent requests, each with its own prefill_len and ring_pos].
+ * Plans the split-KV work for it.  Must not be called in the middle of a
+ * step (after a ring write, before advance: RSWA_E_STATE), nor on a stream
+ * that is being captured into a graph (RSWA_E_STATE: it uploads the plan).
+ * It invalidates graphs captured before it (see rswa_note_steps). */
 int rswa_set_batch(rswa_cache *c, int32_t n, const int32_t *req_ids, void *stream);
 
 /* Ring write for `layer` [section 2.1: in-place overwrite of the ring slot].
@@ -215,8 +220,11 @@ int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out,
 int rswa_decode_step_fused(rswa_cache *c, int32_t layer, const void *q, const void *k_new,
                            const void *v_new, void *out, void *stream);
 
-/* End the step: t += 1 for every active request.  Needs rswa_decode_step of
- * every layer in this step. */
+/* End the step: t += 1 for every active request [section 2.1: after each
+ * generated token the ring position advances by one modulo W,
+ * ring_pos = t mod W, and the cache grows by one entry until it holds
+ * prefill_len + W].  Needs rswa_decode_step of every layer in this step
+ * (RSWA_E_STATE otherwise). */
 int rswa_advance(rswa_cache *c, void *stream);
 
 /* Graph replay of whole decode steps, for callers that capture the
@@ -232,16 +240,23 @@ int rswa_advance(rswa_cache *c, void *stream);
  * no step is half done (RSWA_E_STATE) and that every active request stays
  * below max_positions for k more steps (RSWA_E_POSITION), then advances
  * the host view by k.  Capture only whole steps of one batch, with kernel
- * timing off; rswa_set_batch, rswa_prefill and rswa_get_state must not be
- * captured.  The graph reads the same input and output buffers on every
- * replay; refill them between replays. */
+ * timing off; rswa_set_batch, rswa_prefill, rswa_prefill_chunk and
+ * rswa_get_state refuse a capturing stream (RSWA_E_STATE).  A graph holds
+ * the batch's size, split plan and tables as they were at capture, so
+ * rswa_note_steps also fails with RSWA_E_STATE unless decode work was
+ * captured after the last rswa_set_batch.  The graph reads the same input
+ * and output buffers on every replay; refill them between replays. */
 int rswa_note_steps(rswa_cache *c, int32_t steps);
 
-/* Read the device-side state of n registered requests (host arrays of n).
- * ring_pos = t mod W (slot offset the next step writes), cache_len =
- * P + min(t, W) (valid entries now), next_pos = P + t.  Any output pointer
- * may be NULL.  Synchronizes `stream`; fails with RSWA_E_STATE if the device
- * copy of t differs from the host's. */
+/* Read the device-side state of n registered requests (host arrays of n)
+ * [section 2.1: the next token goes to slot prefill_len + ring_pos with
+ * ring_pos advancing modulo W, and the cache holds at most prefill_len + W
+ * entries].  With t generated tokens cached: ring_pos = t mod W (slot
+ * offset the next step writes), cache_len = P + min(t, W) (valid entries
+ * now), next_pos = P + t (the next token's RoPE position).  Any output
+ * pointer may be NULL.  Synchronizes `stream` (RSWA_E_STATE on a capturing
+ * stream); fails with RSWA_E_STATE if the device copy of t differs from the
+ * host's. */
 int rswa_get_state(rswa_cache *c, int32_t n, const int32_t *req_ids,
                    int32_t *ring_pos, int32_t *cache_len, int32_t *next_pos,
                    void *stream);

@@ -307,7 +307,7 @@ PrefillPlan HostState::plan_prefill(int32_t n, const int32_t *plen, int32_t tile
       if (k < xcd[x].size()) {
         const Item &it = xcd[x][k];
         p.tiles.push_back(it.b);
-        p.tiles.push_back((it.qt << 16) | it.h);
+        p.tiles.push_back((int32_t)(((uint32_t)it.qt << 16) | (uint32_t)it.h));
       } else {
         p.tiles.push_back(-1);
         p.tiles.push_back(0);
@@ -387,6 +387,7 @@ void HostState::commit_set_batch(int32_t n, const int32_t *ids, DecodePlan plan)
   batch_.assign(ids, ids + n);
   for (int32_t id : batch_) in_batch_[id] = 1;
   plan_ = std::move(plan);
+  ++epoch_;
 }
 
 int HostState::check_ring_write(int32_t layer, std::string *err) const {
@@ -446,6 +447,9 @@ int HostState::check_note_steps(int32_t steps, std::string *err) const {
   if (steps < 0) return fail(err, RSWA_E_ARG, "steps must be >= 0");
   if (batch_.empty()) return fail(err, RSWA_E_STATE, "no active batch (rswa_set_batch)");
   if (step_open()) return fail(err, RSWA_E_STATE, "a decode step is half done");
+  if (captured_epoch_ != (int64_t)epoch_)
+    return fail(err, RSWA_E_STATE, "no decode step of the current batch was captured "
+                                   "(rswa_set_batch since the capture invalidates the graph)");
   for (int32_t id : batch_) {
     const RequestState &r = req_[id];
     if ((int64_t)r.plen + r.t + steps > cfg_.max_positions)

@@ -93,7 +93,7 @@ struct PrefillBlob {  // for n requests and t query tiles
   size_t ptot = 0;       // int32 [n]      the request's whole prefill_len
   size_t cu = 0;         // int64 [n + 1]  packed token offset of request b
   size_t base = 0;       // int64 [n]
-  size_t tiles = 0;      // int32 [2t]     launch slots: (b, qt << 16 | head), b < 0 = empty
+  size_t tiles = 0;      // int32 [2t]     launch slots: (b, qt << 16 | head as uint32), b < 0 = empty
   size_t bytes = 0;
   static PrefillBlob make(int n, int64_t t);
   static size_t capacity(const Config &c);
@@ -121,7 +121,7 @@ struct PrefillPlan {
   int32_t max_len = 0;
   std::vector<int64_t> cu;         // n + 1
   // Launch order of (query tile, head) blocks: slot i holds
-  // (b, qt << 16 | head), or b = -1 for an empty slot.  Slot i runs on XCD
+  // (b, qt << 16 | head, packed unsigned), or b = -1 for an empty slot.  Slot i runs on XCD
   // i mod 8; each XCD's slots hold whole (request, head) groups (when there
   // are enough of them) with the longest query tiles first, so blocks that
   // share keys and values run on the same L2.
@@ -185,9 +185,15 @@ class HostState {
   int check_advance(std::string *err) const;
   void commit_advance();
   // `steps` whole decode steps of the current batch ran outside the
-  // library's calls (a replayed graph of them).
+  // library's calls (a replayed graph of them).  Needs a capture of decode
+  // work since the last rswa_set_batch: a graph captured before it holds the
+  // old batch's size, split count and tables.
   int check_note_steps(int32_t steps, std::string *err) const;
   void commit_note_steps(int32_t steps);
+  // Decode work of the current batch was enqueued on a capturing stream.
+  void note_capture() { captured_epoch_ = (int64_t)epoch_; }
+  // Number of rswa_set_batch calls committed so far.
+  uint64_t batch_epoch() const { return epoch_; }
 
   const RequestState &request(int32_t id) const { return req_[id]; }
   const std::vector<int32_t> &batch() const { return batch_; }
@@ -210,6 +216,8 @@ class HostState {
   std::vector<int32_t> batch_;
   DecodePlan plan_;
   std::vector<uint8_t> written_, decoded_;
+  uint64_t epoch_ = 0;           // committed rswa_set_batch calls
+  int64_t captured_epoch_ = -1;  // epoch of the last captured decode work
 };
 
 }  // namespace rswa

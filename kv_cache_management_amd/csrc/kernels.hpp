@@ -68,7 +68,7 @@ struct PrefillArgs {
   const int32_t *ptot;        // [n] the request's whole prefill_len
   const int64_t *cu;          // [n + 1] packed token offsets
   const int64_t *base;        // [n]
-  const int32_t *tiles;       // [2 * num_tiles] launch slots (b, qt << 16 | head); b < 0 empty
+  const int32_t *tiles;       // [2 * num_tiles] launch slots (b, qt << 16 | head as uint32); b < 0 empty
   const void *q;              // [total][H][D]
   const void *k;
   const void *v;

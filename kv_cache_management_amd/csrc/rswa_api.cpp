@@ -28,6 +28,18 @@ int set_global_error(int code, const std::string &msg) {
   return code;
 }
 
+// True while `s` is being captured into a graph.  A failed query (e.g. the
+// legacy stream during another stream's global capture) counts as capturing:
+// the calls that refuse capture then refuse, and launches fail on their own.
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
 }  // namespace
 
 struct rswa_cache {
@@ -275,6 +287,8 @@ int prefill_impl(rswa_cache *c, int32_t layer, int32_t n, const int32_t *req_ids
   std::string err;
   int rc = c->st.check_prefill(layer, n, req_ids, prefill_len, slot_base, &err, chunk_start, chunk_len);
   if (rc != RSWA_OK) return c->fail(rc, err);
+  if (capturing((hipStream_t)stream))
+    return c->fail(RSWA_E_STATE, "prefill uploads its plan and cannot be captured into a graph");
   const Config &cf = c->cfg;
   const int tile = rswa::prefill_tile_rows(cf.dtype, cf.head_dim);
   std::vector<int32_t> qoff(n, 0), rows(prefill_len, prefill_len + n);
@@ -404,6 +418,8 @@ int rswa_set_batch(rswa_cache *c, int32_t n, const int32_t *req_ids, void *strea
     std::string err;
     int rc = c->st.check_set_batch(n, req_ids, &err);
     if (rc != RSWA_OK) return c->fail(rc, err);
+    if (capturing((hipStream_t)stream))
+      return c->fail(RSWA_E_STATE, "rswa_set_batch uploads its plan and cannot be captured into a graph");
     rswa::DecodePlan plan;
     if (n > 0) {
       plan = c->st.plan_decode(n, req_ids);
@@ -444,6 +460,7 @@ int rswa_ring_write(rswa_cache *c, int32_t layer, const void *k_new, const void 
     hipError_t e = rswa::launch_ring_write(a, c->cfg.dtype, c->cfg.head_dim, (hipStream_t)stream);
     if (e != hipSuccess) return c->hip_fail(e, "ring write launch");
     c->st.commit_ring_write(layer);
+    if (capturing((hipStream_t)stream)) c->st.note_capture();
     return RSWA_OK;
   });
 }
@@ -497,6 +514,7 @@ int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, 
   if (e != hipSuccess) return c->hip_fail(e, "decode combine launch");
   if (fused) c->st.commit_fused(layer);
   else c->st.commit_decode(layer);
+  if (capturing(s)) c->st.note_capture();
   return RSWA_OK;
 }
 
@@ -530,6 +548,7 @@ int rswa_advance(rswa_cache *c, void *stream) {
     hipError_t e = rswa::launch_advance(a, (hipStream_t)stream);
     if (e != hipSuccess) return c->hip_fail(e, "advance launch");
     c->st.commit_advance();
+    if (capturing((hipStream_t)stream)) c->st.note_capture();
     return RSWA_OK;
   });
 }
@@ -551,6 +570,8 @@ int rswa_get_state(rswa_cache *c, int32_t n, const int32_t *req_ids, int32_t *ri
   return guarded(c, [&]() -> int {
     const Config &cf = c->cfg;
     if (n < 0 || (n > 0 && !req_ids)) return c->fail(RSWA_E_ARG, "bad n / req_ids");
+    if (capturing((hipStream_t)stream))
+      return c->fail(RSWA_E_STATE, "rswa_get_state synchronizes and cannot be captured into a graph");
     for (int i = 0; i < n; ++i) {
       if (req_ids[i] < 0 || req_ids[i] >= cf.max_requests)
         return c->fail(RSWA_E_ARG, "request id out of range");

@@ -87,7 +87,8 @@ template <> struct Log2<1> { static constexpr int value = 0; };
 // Contiguous layout: the buffer resource starts at the request's first row
 // and ends at the split's last key, so the ragged tail of the last chunk
 // reads zeros without touching memory.  Paged layout: the resource spans the
-// layer; tail keys reuse the last valid key's row and get probability 0.
+// layer; tail keys reuse the last valid key's row, get probability 0 and
+// have their value registers zeroed.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(256, RSWA_DECODE_MIN_BLOCKS) void decode_split_kernel(DecodeArgs a) {
@@ -279,6 +280,16 @@ __global__ __launch_bounds__(256, RSWA_DECODE_MIN_BLOCKS) void decode_split_kern
     }
     __builtin_amdgcn_wave_barrier();
     patch(vr, c0, 1);
+    // Paged tail: keys past the split's end loaded the row of its last key
+    // (possibly the row this wave has just written); their weight is 0, and
+    // zeroed values keep 0 * v finite whatever that row held.
+    if constexpr (PAGED) {
+      if (!more) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          if (c0 + i * TPI + g >= end) vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
     // Key i * TPI + g is scored by lanes g * LPR + (i << SH) ...
 #pragma unroll
     for (int i = 0; i < NI; ++i) {

@@ -139,8 +139,9 @@ __global__ __launch_bounds__(64) void prefill_attn_valu_kernel(PrefillArgs a) {
   __shared__ float vs[KT][D];
   const int b = a.tiles[2 * blockIdx.x];
   if (b < 0) return;  // empty launch slot
-  const int qt = a.tiles[2 * blockIdx.x + 1] >> 16;
-  const int h = a.tiles[2 * blockIdx.x + 1] & 0xffff;
+  const uint32_t slot = (uint32_t)a.tiles[2 * blockIdx.x + 1];  // qt << 16 | head, unsigned
+  const int qt = (int)(slot >> 16);
+  const int h = (int)(slot & 0xffffu);
   const int c_len = a.plen[b];   // rows of this chunk
   const int q_off = a.qoff[b];   // position of its first row
   const int64_t base = a.base[b];

@@ -116,8 +116,9 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
 
   const int b = a.tiles[2 * blockIdx.x];
   if (b < 0) return;  // empty launch slot
-  const int qt = a.tiles[2 * blockIdx.x + 1] >> 16;
-  const int h = a.tiles[2 * blockIdx.x + 1] & 0xffff;
+  const uint32_t slot = (uint32_t)a.tiles[2 * blockIdx.x + 1];  // qt << 16 | head, unsigned
+  const int qt = (int)(slot >> 16);
+  const int h = (int)(slot & 0xffffu);
   const int c_len = a.plen[b];   // query rows of this call (a chunk of the prefill)
   const int q_off = a.qoff[b];   // position of the chunk's first row
   const int64_t base = a.base[b];

@@ -276,7 +276,10 @@ static void test_fused_step() {
   CHECK(st.check_advance(&err) == RSWA_OK);
   st.commit_advance();
   CHECK(st.request(1).t == 1);
-  // graph replay bookkeeping: whole steps only, positions checked
+  // graph replay bookkeeping: whole steps only, positions checked, and only
+  // for a graph captured since the last rswa_set_batch
+  CHECK(st.check_note_steps(3, &err) == RSWA_E_STATE);  // nothing captured
+  st.note_capture();
   CHECK(st.check_note_steps(3, &err) == RSWA_OK);
   st.commit_note_steps(3);
   CHECK(st.request(1).t == 4);
@@ -291,6 +294,46 @@ static void test_fused_step() {
   const int32_t room = st.config().max_positions - (7 + 5);
   CHECK(st.check_note_steps(room, &err) == RSWA_OK);
   CHECK(st.check_note_steps(room + 1, &err) == RSWA_E_POSITION);
+  // a new batch (even the same ids) invalidates the captured graph
+  const uint64_t e0 = st.batch_epoch();
+  CHECK(st.check_set_batch(1, ids, &err) == RSWA_OK);
+  st.commit_set_batch(1, ids, st.plan_decode(1, ids));
+  CHECK(st.batch_epoch() == e0 + 1);
+  CHECK(st.check_note_steps(1, &err) == RSWA_E_STATE);
+  st.note_capture();
+  CHECK(st.check_note_steps(1, &err) == RSWA_OK);
+}
+
+// Query-tile indices up to 65535 (64-row tiles of a 4194304-position prefill)
+// survive the (qt << 16 | head) packing when unpacked unsigned.
+static void test_prefill_tile_index_limit() {
+  rswa_config rc = base_cfg();
+  rc.num_heads = 1;
+  rc.head_dim = 64;
+  rc.dtype = RSWA_DTYPE_F32;
+  rc.window = 1;
+  rc.max_requests = 1;
+  rc.max_positions = 1 << 22;
+  rc.num_slots = (1 << 22) + 1;
+  rc.max_prefill_tokens = 1 << 22;
+  Config c = resolved(rc);
+  HostState st(c);
+  int32_t len[1] = {1 << 22};
+  PrefillPlan pp = st.plan_prefill(1, len, 64);
+  std::vector<uint8_t> seen(65536, 0);
+  int64_t items = 0;
+  for (int64_t i = 0; i < pp.num_tiles(); ++i) {
+    if (pp.tiles[2 * i] < 0) continue;
+    const uint32_t slot = (uint32_t)pp.tiles[2 * i + 1];
+    const uint32_t qt = slot >> 16, h = slot & 0xffffu;
+    CHECK(h == 0);
+    CHECK(qt < 65536);
+    if (qt < 65536) seen[qt] += 1;
+    ++items;
+  }
+  CHECK(items == 65536);
+  CHECK(std::count(seen.begin(), seen.end(), 1) == 65536);
+  CHECK(pp.num_tiles() <= c.max_prefill_blocks());
 }
 
 static void test_decode_plan() {
@@ -450,6 +493,7 @@ int main() {
   test_prefill_xcd_plan();
   test_step_machine_and_ring();
   test_fused_step();
+  test_prefill_tile_index_limit();
   test_decode_plan();
   test_chunked_prefill();
   test_admission();

@@ -1,8 +1,10 @@
 """Graph replay of whole decode steps (rswa_note_steps): a captured graph of
 K fused decode steps + advance, replayed several times with fresh inputs
 copied into its buffers and eager work between replays, gives bit-identical
-outputs and state to the same steps run eagerly on a second cache, and the
-eager path itself matches the oracle."""
+outputs and state to the same steps run eagerly on a second cache; the state
+of both is checked against the oracle's closed forms for ring_pos, cache_len
+and position.  The fused eager outputs themselves are compared with the
+oracle's RingCache in test_gpu_parity.py (test_fused_ring_write_decode)."""
 
 import numpy as np
 import pytest
@@ -89,8 +91,28 @@ def test_graph_replay_matches_eager(paged):
             assert np_g[b] == O.position(p, t)
     # the host view kept pace: a further whole-step call is accepted
     gcache.note_steps(0)
+    # a new batch (the same ids) invalidates the graph captured before it
+    gcache.set_batch(list(range(n)))
+    with pytest.raises(R.RSWAError) as e:
+        gcache.note_steps(K)
+    assert e.value.status == R.RSWA_E_STATE
     for c in caches:
         c.close()
+
+
+def _capture_one_step(torch, c, layers, z, zo):
+    """Captures one whole fused step of c's batch into a graph (not replayed)."""
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for l in range(layers):
+                c.decode_step_fused(l, z, z, z, zo)
+            c.advance()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return graph
 
 
 def test_note_steps_rejects_half_step_and_position_overflow():
@@ -106,14 +128,30 @@ def test_note_steps_rejects_half_step_and_position_overflow():
     c.set_batch([0])
     z = torch.zeros((1, 2, 64), device=dev, dtype=torch.bfloat16)
     zo = torch.empty_like(z)
+    with pytest.raises(R.RSWAError) as e:  # nothing captured for this batch
+        c.note_steps(1)
+    assert e.value.status == R.RSWA_E_STATE
+    graph = _capture_one_step(torch, c, 2, z, zo)  # counts as step 0
     c.decode_step_fused(0, z, z, z, zo)
-    with pytest.raises(R.RSWAError) as e:
+    with pytest.raises(R.RSWAError) as e:  # step 1 half done
         c.note_steps(1)
     assert e.value.status == R.RSWA_E_STATE
     c.decode_step_fused(1, z, z, z, zo)
     c.advance()
-    c.note_steps(4096 - 10 - 1)
+    c.note_steps(4096 - 10 - 2)
     with pytest.raises(R.RSWAError) as e:
         c.note_steps(1)
     assert e.value.status == R.RSWA_E_POSITION
+    # calls that upload or synchronize refuse a capturing stream
+    g2 = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    codes = []
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g2, stream=side):
+            codes.append(R.rswa_set_batch(c.handle, [0], side.cuda_stream))
+            codes.append(R.rswa_get_state(c.handle, [0], side.cuda_stream)[0])
+    torch.cuda.synchronize()
+    assert codes == [R.RSWA_E_STATE, R.RSWA_E_STATE]
+    del graph, g2
     c.close()
