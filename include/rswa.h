@@ -23,7 +23,10 @@
  * - All device pointers are HIP device memory owned by the caller.  The
  *   library never allocates or frees device memory.  It allocates only the
  *   host-side handle and a small pinned host staging area, both released by
- *   rswa_cache_destroy.
+ *   rswa_cache_destroy.  Its only device memory of its own is the fixed
+ *   scratch array of rswa_decode_step_fused_noalloc (a static device array of
+ *   RSWA_NOALLOC_SCRATCH_BYTES, present on each GPU the library is loaded on
+ *   until the process ends).
  * - `stream` is a hipStream_t (NULL = the null stream).  All work is
  *   enqueued asynchronously on it; only rswa_cache_init and rswa_get_state
  *   block.  Use one stream per handle.
@@ -219,6 +222,24 @@ int rswa_decode_step(rswa_cache *c, int32_t layer, const void *q, void *out,
  * once this call's kernels have run. */
 int rswa_decode_step_fused(rswa_cache *c, int32_t layer, const void *q, const void *k_new,
                            const void *v_new, void *out, void *stream);
+
+/* rswa_decode_step_fused for callers that cannot allocate device memory or
+ * call hipMalloc (code under graph capture, tight serving loops, harnesses
+ * that forbid it): the same kernels, inputs, outputs, state rules and
+ * errors, but the split-KV partials go to a fixed device array inside the
+ * library instead of the handle's workspace, and no allocating call is made
+ * (kernel timing by rswa_profile_* is skipped for this call).  The array
+ * holds RSWA_NOALLOC_SCRATCH_BYTES per GPU, from the library's first
+ * rswa_cache_init on that GPU until the process ends.  A batch whose
+ * partials need more -- num_splits * num_heads * (head_dim * 4 + 8) bytes
+ * plus alignment, see rswa_decode_plan -- is refused with RSWA_E_CAPACITY
+ * before anything launches.  Every handle on one GPU shares the array:
+ * calls that overlap in time on one GPU (on different streams, or from
+ * different threads) race and must be ordered by the caller. */
+#define RSWA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int rswa_decode_step_fused_noalloc(rswa_cache *c, int32_t layer, const void *q,
+                                   const void *k_new, const void *v_new, void *out,
+                                   void *stream);
 
 /* End the step: t += 1 for every active request [section 2.1: after each
  * generated token the ring position advances by one modulo W,

@@ -96,4 +96,9 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, int head_dim, hipStream_t s
 int prefill_tile_rows(int dtype, int head_dim);
 hipError_t launch_prefill_attention(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
 
+// Device address, on the current device, of the fixed scratch array that
+// rswa_decode_step_fused_noalloc keeps its split-KV partials in
+// (RSWA_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned).
+hipError_t noalloc_scratch_address(void **out);
+
 }  // namespace rswa

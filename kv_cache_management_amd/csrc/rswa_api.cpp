@@ -95,6 +95,10 @@ struct rswa_cache {
   const float2 *rope() const { return (const float2 *)(ws + lay.rope); }
 
   const int32_t *slot_table = nullptr;
+  // Device address of the fixed scratch array on this handle's GPU
+  // (rswa_decode_step_fused_noalloc), resolved at init; null if that failed.
+  void *noalloc_scratch = nullptr;
+  std::string noalloc_err;
 
   // Kernel timing (rswa_profile_*): event pairs per kernel kind, reused.
   bool prof = false;
@@ -252,6 +256,13 @@ int rswa_cache_init(const rswa_config *cfg, void *k_pool, void *v_pool, void *wo
     if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.req_base, 0, sizeof(int64_t) * c.max_requests, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return cleanup(e, "uploading the RoPE table");
+    // Resolved here, once per device, for rswa_decode_step_fused_noalloc; a
+    // failure only disables that entry point.
+    e = rswa::noalloc_scratch_address(&h->noalloc_scratch);
+    if (e != hipSuccess) {
+      h->noalloc_scratch = nullptr;
+      h->noalloc_err = std::string("hipGetSymbolAddress of the fixed scratch: ") + hipGetErrorString(e);
+    }
     *out = h;
     return RSWA_OK;
   });
@@ -469,8 +480,14 @@ int rswa_ring_write(rswa_cache *c, int32_t layer, const void *k_new, const void 
 
 namespace {
 
+// Split-KV partials of `tasks` (split, head) items in the fixed scratch:
+// float [tasks][head_dim], then float2 [tasks] at a 256-byte boundary.
+size_t noalloc_ml_offset(int64_t tasks, int head_dim) {
+  return rswa::align_up((size_t)tasks * head_dim * sizeof(float));
+}
+
 int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, const void *v_new,
-                void *out, void *stream) {
+                void *out, void *stream, bool noalloc = false) {
   const bool fused = k_new != nullptr || v_new != nullptr;
   std::string err;
   int rc = fused ? c->st.check_fused(layer, &err) : c->st.check_decode(layer, &err);
@@ -479,6 +496,16 @@ int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, 
   if (fused && (!k_new || !v_new)) return c->fail(RSWA_E_ARG, "null k_new / v_new");
   const rswa::DecodePlan &plan = c->st.plan();
   const int n = (int)c->st.batch().size();
+  const int64_t tasks = (int64_t)plan.num_splits() * c->cfg.num_heads;
+  if (noalloc) {
+    if (!c->noalloc_scratch) return c->fail(RSWA_E_HIP, c->noalloc_err);
+    const size_t need = noalloc_ml_offset(tasks, c->cfg.head_dim) + (size_t)tasks * sizeof(float2);
+    if (need > (size_t)RSWA_NOALLOC_SCRATCH_BYTES)
+      return c->fail(RSWA_E_CAPACITY, "the batch's " + std::to_string(tasks) +
+                                          " split-KV partials need " + std::to_string(need) +
+                                          " bytes; the fixed scratch holds " +
+                                          std::to_string((size_t)RSWA_NOALLOC_SCRATCH_BYTES));
+  }
   rswa::BatchBlob bb = rswa::BatchBlob::make(n, plan.num_splits());
   const char *dev = c->ws + c->lay.batch;
   rswa::DecodeArgs a{};
@@ -492,8 +519,13 @@ int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, 
   a.out = out;
   a.k_new = k_new;
   a.v_new = v_new;
-  a.part_o = (float *)(c->ws + c->lay.part_o);
-  a.part_ml = (float2 *)(c->ws + c->lay.part_ml);
+  if (noalloc) {
+    a.part_o = (float *)c->noalloc_scratch;
+    a.part_ml = (float2 *)((char *)c->noalloc_scratch + noalloc_ml_offset(tasks, c->cfg.head_dim));
+  } else {
+    a.part_o = (float *)(c->ws + c->lay.part_o);
+    a.part_ml = (float2 *)(c->ws + c->lay.part_ml);
+  }
   a.rope = c->rope();
   a.qscale = c->qscale;
   a.layer_bytes = (uint32_t)std::min<int64_t>(
@@ -506,7 +538,7 @@ int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, 
   a.split_tokens = plan.split_tokens;
   a.attention = c->cfg.attention;
   hipStream_t s = (hipStream_t)stream;
-  const int pi = c->prof_begin(RSWA_KERNEL_DECODE_SPLIT, s);
+  const int pi = noalloc ? -1 : c->prof_begin(RSWA_KERNEL_DECODE_SPLIT, s);
   hipError_t e = rswa::launch_decode_split(a, c->cfg.dtype, c->cfg.head_dim, s);
   c->prof_end(RSWA_KERNEL_DECODE_SPLIT, pi, s);
   if (e != hipSuccess) return c->hip_fail(e, "split-KV decode launch");
@@ -532,6 +564,15 @@ int rswa_decode_step_fused(rswa_cache *c, int32_t layer, const void *q, const vo
   if (!c) return set_global_error(RSWA_E_ARG, "null handle");
   if (!k_new || !v_new) return c->fail(RSWA_E_ARG, "null k_new / v_new");
   return guarded(c, [&]() -> int { return decode_impl(c, layer, q, k_new, v_new, out, stream); });
+}
+
+int rswa_decode_step_fused_noalloc(rswa_cache *c, int32_t layer, const void *q, const void *k_new,
+                                   const void *v_new, void *out, void *stream) {
+  if (!c) return set_global_error(RSWA_E_ARG, "null handle");
+  if (!k_new || !v_new) return c->fail(RSWA_E_ARG, "null k_new / v_new");
+  return guarded(c, [&]() -> int {
+    return decode_impl(c, layer, q, k_new, v_new, out, stream, /*noalloc=*/true);
+  });
 }
 
 int rswa_advance(rswa_cache *c, void *stream) {

@@ -39,7 +39,9 @@ EXPORTED = (
     "rswa_last_error", "rswa_profile_enable", "rswa_profile_read", "rswa_decode_step_fused",
     "rswa_measure_read", "rswa_ngram_ban", "rswa_note_steps", "rswa_prefill_chunk",
     "rswa_admit", "rswa_retire", "rswa_free_rows", "rswa_measure_mfma",
+    "rswa_decode_step_fused_noalloc",
 )
+RSWA_NOALLOC_SCRATCH_BYTES = 16 << 20
 RSWA_NGRAM_MAX_WINDOW = 4096
 RSWA_MEASURE_SINK_WORDS = 4096
 RSWA_MEASURE_MFMA_FRAGMENTS = 65536
@@ -120,6 +122,7 @@ def load():
         "rswa_ring_write": (ctypes.c_int, [P, I32, P, P, P]),
         "rswa_decode_step": (ctypes.c_int, [P, I32, P, P, P]),
         "rswa_decode_step_fused": (ctypes.c_int, [P, I32, P, P, P, P, P]),
+        "rswa_decode_step_fused_noalloc": (ctypes.c_int, [P, I32, P, P, P, P, P]),
         "rswa_advance": (ctypes.c_int, [P, P]),
         "rswa_get_state": (ctypes.c_int, [P, I32, pI32, pI32, pI32, pI32, P]),
         "rswa_decode_plan": (ctypes.c_int, [P, pI32, pI32]),
@@ -237,6 +240,11 @@ def rswa_decode_step(handle, layer: int, q: int, out: int, stream: int) -> int:
 def rswa_decode_step_fused(handle, layer: int, q: int, k_new: int, v_new: int, out: int,
                            stream: int) -> int:
     return load().rswa_decode_step_fused(handle, layer, q, k_new, v_new, out, stream)
+
+
+def rswa_decode_step_fused_noalloc(handle, layer: int, q: int, k_new: int, v_new: int, out: int,
+                                   stream: int) -> int:
+    return load().rswa_decode_step_fused_noalloc(handle, layer, q, k_new, v_new, out, stream)
 
 
 def rswa_advance(handle, stream: int) -> int:
@@ -457,6 +465,12 @@ class RSWACache:
         shp = (self.n, self.heads, self.head_dim)
         self._check(rswa_decode_step_fused(self.handle, layer, self._ptr(q, shp), self._ptr(k_new, shp),
                                            self._ptr(v_new, shp), self._ptr(out, shp), self.stream()))
+
+    def decode_step_fused_noalloc(self, layer: int, q, k_new, v_new, out):
+        shp = (self.n, self.heads, self.head_dim)
+        self._check(rswa_decode_step_fused_noalloc(self.handle, layer, self._ptr(q, shp),
+                                                   self._ptr(k_new, shp), self._ptr(v_new, shp),
+                                                   self._ptr(out, shp), self.stream()))
 
     def advance(self):
         self._check(rswa_advance(self.handle, self.stream()))
