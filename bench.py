@@ -5,9 +5,12 @@
 One step is one whole job of the workload through the C ABI: causal prefill
 of every request in every layer (RoPE + cache write + attention), the
 staggered pre-roll that puts requests at different ring phases, then the
-measured decode steps (per layer: ring write + split-KV decode + combine;
-then advance).  Inputs are synthetic and already resident in HBM when timing
-starts.  Prints one JSON line.
+measured decode steps (per layer one launch: ring write, split-KV decode and
+the cross-split merge; the step's last layer also advances the ring state).
+Inputs are synthetic and already resident in HBM when timing starts.  The
+timed steps carry no per-launch instrumentation; kernel durations for the
+roofline come from one more job with event pairs around each launch.
+Prints one JSON line.
 
 value = decode KV-read GB/s over the measured decode steps: per request,
 layer and step the method must read 4 * H * D * L bytes of bf16 keys and
@@ -272,22 +275,28 @@ class Job:
         return ms, cnt
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per decode-split launch from the committed PMC summary, if it
-    was taken on the current kernel source; else None."""
+def traffic_from_profile(workload: str, algorithmic_bytes_per_launch: float):
+    """HBM traffic per decode launch from the committed PMC summary of this
+    workload: (bytes, record) when it was taken on the current kernel source
+    and on launches with the same algorithmic bytes as this line's (the same
+    steps of the same workload), else (None, reason)."""
     path = os.path.join(PROFILE_DIR, f"decode_split_{workload}_pmc.md")
     if not os.path.exists(path):
-        return None
+        return None, f"no {os.path.basename(path)}"
     from kv_cache_management_amd.profsummary import kernel_source_sha
 
-    sha = kernel_source_sha("decode_split")
     rec = None
     for line in open(path):
         if line.startswith("<!-- traffic "):
             rec = json.loads(line[len("<!-- traffic "):].rsplit("-->", 1)[0])
-    if not rec or rec.get("kernel_source_sha256_16") != sha:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    if not rec:
+        return None, "no traffic record"
+    if rec.get("kernel_source_sha256_16") != kernel_source_sha("decode_split"):
+        return None, "decode kernel changed since the counters were taken"
+    alg = rec.get("algorithmic_bytes_per_launch", 0)
+    if abs(alg - algorithmic_bytes_per_launch) > 1e-6 * algorithmic_bytes_per_launch:
+        return None, "counters were taken on other launches (different algorithmic bytes)"
+    return rec.get("hbm_bytes_per_launch"), rec
 
 
 def measured_peaks(torch, rswa, read_gib: int = 4):
@@ -537,15 +546,26 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0, attention: str = "rswa")
     from kv_cache_management_amd import synth
     from oracle import rswa_oracle as O
 
+    # Every core this process may run on, with the BLAS pool set to match.
+    cores = len(os.sched_getaffinity(0))
     blas = None
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
         info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        cores = sum(i.get("num_threads", 0) for i in info) or 1
         if info:
-            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            blas = {"library": info[0].get("internal_api"), "version": info[0].get("version"),
+                    "threads": info[0].get("num_threads"), "arch": info[0].get("architecture")}
     except Exception:
-        cores = 1
+        pass
+    try:
+        np_cfg = np.show_config(mode="dicts")
+        np_build = {"blas": np_cfg.get("Build Dependencies", {}).get("blas", {}).get("name"),
+                    "lapack": np_cfg.get("Build Dependencies", {}).get("lapack", {}).get("name"),
+                    "simd": np_cfg.get("SIMD Extensions", {}).get("found")}
+    except Exception:
+        np_build = None
     n = w.batch
     reqs = sorted(set(np.linspace(0, n - 1, min(8, n)).round().astype(int).tolist()))
     starts = w.starts()
@@ -588,6 +608,8 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0, attention: str = "rswa")
     O.prefill(q, k, v, w.rope_base)
     t_pf = time.perf_counter() - t0
     pf_flops = O.prefill_flops(p, w.heads, w.head_dim)
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {
         "value": round(kv / t_dec / 1e9, 4),
         "unit": "GB/s",
@@ -597,7 +619,9 @@ def cpu_baseline(w: W.Workload, budget_s: float = 16.0, attention: str = "rswa")
                    f"requests {reqs} in layer {layer} ({kv / 1e9:.3f} GB of algorithmic KV reads "
                    f"in {t_dec:.2f} s); prefill: one request, first {p} tokens, layer {layer}"),
         "cpu": cpu_model(),
+        "cores_source": "len(os.sched_getaffinity(0)); BLAS threads set to it",
         "blas": blas,
+        "numpy_build": np_build,
         "decode_steps_per_s_per_request_layer": round(steps_done / t_dec, 3),
         "prefill_gflops": round(pf_flops / t_pf / 1e9, 3),
     }
@@ -695,8 +719,10 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     pf_ms, dec_ms = [], []
+    # The timed steps carry no per-launch events (only the bracket, and with
+    # --cold one pair per decode step).
     for i in range(args.steps):
-        job.run(profile_kernels=prof)
+        job.run(profile_kernels=False)
         a, b = job.times_ms()   # events of this step: synchronizes on them
         pf_ms.append(a)
         dec_ms.append(b)
@@ -716,8 +742,17 @@ def main():
                       "max_ms": round(float(st_ms.max()), 4),
                       "last_quarter_over_first_quarter": round(float(st_ms[-q:].mean() / st_ms[:q].mean()), 4),
                       "steps": int(len(st_ms)), "run": "last measured job"}
-    k_dec = job.kernel_time(rswa.RSWA_KERNEL_DECODE_SPLIT) if prof else (None, 0)
-    k_pf = job.kernel_time(rswa.RSWA_KERNEL_PREFILL_ATTENTION) if prof else (None, 0)
+    k_dec = k_pf = (None, 0)
+    if prof:
+        # Kernel durations: one more job of the same work with an event pair
+        # around every decode and prefill-attention launch (eager calls).
+        log("kernel-timing job")
+        graph_k, job.graph_k = job.graph_k, 0
+        job.run(profile_kernels=True)
+        job.times_ms()
+        job.graph_k = graph_k
+        k_dec = job.kernel_time(rswa.RSWA_KERNEL_DECODE_SPLIT)
+        k_pf = job.kernel_time(rswa.RSWA_KERNEL_PREFILL_ATTENTION)
 
     dec_s = sum(dec_ms) / 1e3
     kv_total = job.kv_bytes * args.steps
@@ -729,12 +764,15 @@ def main():
         per_launch_bytes = job.kv_bytes / job.kv_launches
         avg_s = k_dec[0] / k_dec[1] / 1e3
         achieved = per_launch_bytes / avg_s / 1e9
-        traffic = traffic_from_profile(w.name)
+        traffic, trec = traffic_from_profile(w.name, per_launch_bytes)
         roofline = {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic,
+                    "traffic_over_algorithmic": (round(traffic / per_launch_bytes, 4) if traffic else None),
+                    "traffic_note": (f"profiles/decode_split_{w.name}_pmc.md" if traffic else trec),
                     "algorithmic_bytes_per_launch": int(per_launch_bytes),
-                    "avg_launch_us": round(avg_s * 1e6, 2), "launches": k_dec[1]}
+                    "avg_launch_us": round(avg_s * 1e6, 2), "launches": k_dec[1],
+                    "timing": "HIP event pair per launch, in a separate job after the timed steps"}
     prefill_kernel = None
     if prof and k_pf[1]:
         avg_s = k_pf[0] / k_pf[1] / 1e3

@@ -94,8 +94,8 @@ BatchBlob BatchBlob::make(int n, int k) {
   BatchBlob b;
   b.req = 0;
   b.split_off = align_up(sizeof(int32_t) * n, 16);
-  b.split_map = b.split_off + align_up(sizeof(int32_t) * (n + 1), 16);
-  b.bytes = b.split_map + align_up(sizeof(int32_t) * 2 * (size_t)k, 16);
+  b.splits = b.split_off + align_up(sizeof(int32_t) * (n + 1), 32);
+  b.bytes = b.splits + sizeof(SplitDesc) * (size_t)k;
   return b;
 }
 
@@ -134,6 +134,8 @@ Layout make_layout(const Config &c) {
   L.batch = take(L.batch_bytes);
   L.part_o = take(sizeof(float) * (size_t)c.max_splits * c.num_heads * c.head_dim);
   L.part_ml = take(sizeof(float) * 2 * (size_t)c.max_splits * c.num_heads);
+  L.merge_cnt = take(sizeof(int32_t) * (size_t)c.max_requests * c.num_heads);
+  L.step_cnt = take(sizeof(int32_t) * (size_t)c.max_requests);
   L.prefill_bytes = PrefillBlob::capacity(c);
   L.prefill = take(L.prefill_bytes);
   L.total = off;
@@ -347,36 +349,47 @@ DecodePlan HostState::plan_decode(int32_t n, const int32_t *ids) const {
   // Key range a request's decode steps can reach: logical slots
   // decode_key0(P) .. P + W - 1 (all of 0 .. P + W - 1 for R-SWA).
   std::vector<int64_t> lmax(n);
-  int64_t sum = 0;
+  int64_t longest = 0;
   for (int b = 0; b < n; ++b) {
-    const int32_t p = req_[ids[b]].plen;
-    lmax[b] = (int64_t)p + cfg_.window - decode_key0(p);
-    sum += lmax[b];
+    const int32_t pl = req_[ids[b]].plen;
+    lmax[b] = (int64_t)pl + cfg_.window - decode_key0(pl);
+    longest = std::max(longest, lmax[b]);
   }
-  int64_t s;
-  if (cfg_.decode_split_tokens > 0) {
-    s = cfg_.decode_split_tokens;
-  } else {
-    auto round64 = [](int64_t x) { return std::max<int64_t>(kSplitQuantum, ceil_div(x, kSplitQuantum) * kSplitQuantum); };
-    const int64_t work = sum * cfg_.num_heads;
-    const int64_t fill = round64(ceil_div(work, kWaveSlots));
-    s = std::max(round64(ceil_div(work, kDefaultTargetTasks)),
-                 std::min<int64_t>(kPreferredSplit, fill));
-    auto count = [&](int64_t sz) {
-      int64_t k = 0;
-      for (int b = 0; b < n; ++b) k += ceil_div(lmax[b], sz);
-      return k;
-    };
-    while (count(s) > cfg_.max_splits) s += kSplitQuantum;
+  const int64_t heads = cfg_.num_heads;
+  auto splits_of = [&](int64_t sz) {
+    int64_t k = 0;
+    for (int b = 0; b < n; ++b) k += ceil_div(lmax[b], sz);
+    return k;
+  };
+  int64_t keys = 0;
+  for (int b = 0; b < n; ++b) keys += lmax[b];
+  int64_t sz = cfg_.decode_split_tokens;
+  if (sz <= 0) {
+    if (keys * heads <= kOneRoundKeys) {
+      sz = kSplitQuantum;
+      while (splits_of(sz) * heads > kDecodeWaves) sz += kSplitQuantum;
+    } else {
+      sz = kLongSplitKeys;
+    }
+    while (splits_of(sz) > cfg_.max_splits) sz += kSplitQuantum;
   }
-  p.split_tokens = (int32_t)s;
+  p.split_tokens = (int32_t)std::min<int64_t>(sz, longest);
   p.split_off.assign(n + 1, 0);
   for (int b = 0; b < n; ++b) {
-    int32_t k = (int32_t)ceil_div(lmax[b], s);
-    p.split_off[b + 1] = p.split_off[b] + k;
-    for (int32_t j = 0; j < k; ++j) {
-      p.split_map.push_back(b);
-      p.split_map.push_back(j);
+    const int32_t id = ids[b];
+    const RequestState &rq = req_[id];
+    const int64_t k = ceil_div(lmax[b], sz);
+    const int64_t key0 = decode_key0(rq.plen);
+    p.split_off[b + 1] = p.split_off[b] + (int32_t)k;
+    for (int64_t j = 0; j < k; ++j) {
+      SplitDesc d{};
+      d.b = b;
+      d.r = id;
+      d.k0 = (int32_t)(key0 + j * sz);
+      d.k1 = (int32_t)std::min(key0 + (j + 1) * sz, key0 + lmax[b]);
+      d.p = rq.plen;
+      d.base = rq.base;
+      p.splits.push_back(d);
     }
   }
   return p;
@@ -435,6 +448,18 @@ int HostState::check_advance(std::string *err) const {
     if (!decoded_[l])
       return fail(err, RSWA_E_STATE, "layer " + S(l) + " not decoded in this step");
   return RSWA_OK;
+}
+
+bool HostState::completes_step(int32_t layer) const {
+  for (int l = 0; l < cfg_.num_layers; ++l)
+    if (l != layer && !decoded_[l]) return false;
+  return !decoded_[layer];
+}
+
+bool HostState::step_decoded() const {
+  for (int l = 0; l < cfg_.num_layers; ++l)
+    if (!decoded_[l]) return false;
+  return !batch_.empty();
 }
 
 void HostState::commit_advance() {

@@ -21,17 +21,20 @@
 namespace rswa {
 
 constexpr int kAlign = 256;
-constexpr int kSplitQuantum = 64;      // split sizes are multiples of this
-// Split-KV planning (measured on MI355X): aim for about two rounds of
-// decode wavefronts (3 resident per SIMD x 4 SIMDs x 256 CUs = 3072 per
-// round), but do not cut splits below 256 keys when the batch fills one
-// round at that size.
-#ifndef RSWA_TARGET_TASKS
-#define RSWA_TARGET_TASKS 6144
-#endif
-constexpr int kDefaultTargetTasks = RSWA_TARGET_TASKS;
-constexpr int kWaveSlots = 3072;
-constexpr int kPreferredSplit = 256;
+constexpr int kSplitQuantum = 64;      // forced split sizes are multiples of this
+// Split-KV planning (measured on MI355X).  A decode step streams at the
+// rate its busiest CU allows, and each wave adds a fixed start-up and merge
+// latency.  Splits are kSplitQuantum-multiples (the last split of a request
+// takes the remainder; equal splits at arbitrary key offsets measured
+// slower).  Batches of at most kOneRoundKeys key-heads run as one round of
+// at most kDecodeWaves waves (one per SIMD, blocks of four, at most one
+// block per CU), with the shortest split length that fits; larger batches use
+// kLongSplitKeys-key splits.
+constexpr int kDecodeWaves = 1024;          // 256 CUs x 4 SIMDs
+constexpr int kDecodeWavesPerBlock = 4;
+constexpr int kDecodeCUs = 256;
+constexpr int kLongSplitKeys = 1024;
+constexpr int64_t kOneRoundKeys = (int64_t)kDecodeWaves * 1280;
 constexpr int kDefaultMaxPositions = 32768;
 constexpr int64_t kDefaultMaxPrefillTokens = 262144;
 constexpr int kPrefillTileMin = 64;    // smallest prefill query tile of any kernel
@@ -66,6 +69,8 @@ struct Layout {
   size_t batch_bytes = 0;
   size_t part_o = 0;      // float [max_splits][num_heads][head_dim]
   size_t part_ml = 0;     // float2 [max_splits][num_heads]  (max, sum)
+  size_t merge_cnt = 0;   // int32 [max_requests][num_heads]  splits finished per (entry, head)
+  size_t step_cnt = 0;    // int32 [max_requests]  heads merged per entry (step's last layer)
   size_t prefill = 0;     // prefill blob (see PrefillBlob)
   size_t prefill_bytes = 0;
   size_t total = 0;
@@ -76,11 +81,20 @@ struct Layout {
 int resolve_config(const rswa_config &in, Config *out, std::string *err);
 Layout make_layout(const Config &c);
 
+// One split-KV work item: keys [k0, k1) (logical slots) of batch entry b,
+// request r with prefill_len p and first pool row / table index base.
+// k1 <= p + W; the keys a step reads are the part below p + min(t + 1, W).
+struct SplitDesc {
+  int32_t b, r, k0, k1, p, pad;
+  int64_t base;
+};
+static_assert(sizeof(SplitDesc) == 32, "split descriptor is one 32-byte scalar load");
+
 // Offsets inside a packed blob uploaded in one copy.
 struct BatchBlob {   // for n active requests and k split work items
   size_t req = 0;        // int32 [n]      request id of batch entry b
   size_t split_off = 0;  // int32 [n + 1]  first split of batch entry b
-  size_t split_map = 0;  // int32 [2k]     (b, split index within b)
+  size_t splits = 0;     // SplitDesc [k]
   size_t bytes = 0;
   static BatchBlob make(int n, int k);
   static size_t capacity(const Config &c);
@@ -106,10 +120,10 @@ struct RequestState {
 };
 
 struct DecodePlan {
-  int32_t split_tokens = 0;
+  int32_t split_tokens = 0;        // keys of the longest split
   std::vector<int32_t> split_off;  // n + 1
-  std::vector<int32_t> split_map;  // 2 * num_splits
-  int32_t num_splits() const { return (int32_t)split_map.size() / 2; }
+  std::vector<SplitDesc> splits;   // num_splits, entry-major
+  int32_t num_splits() const { return (int32_t)splits.size(); }
 };
 
 constexpr int kNumXcds = 8;            // MI355X: workgroup i runs on XCD i mod 8
@@ -184,6 +198,13 @@ class HostState {
   void commit_fused(int32_t layer);
   int check_advance(std::string *err) const;
   void commit_advance();
+  // The decode of `layer` completes this step's set of decoded layers, so
+  // its kernel also advances the device copy of t (rswa_advance then only
+  // updates the host view).
+  bool completes_step(int32_t layer) const;
+  // Every layer of the open step is decoded: the device t of the batch is
+  // already one ahead of the host's until rswa_advance.
+  bool step_decoded() const;
   // `steps` whole decode steps of the current batch ran outside the
   // library's calls (a replayed graph of them).  Needs a capture of decode
   // work since the last rswa_set_batch: a graph captured before it holds the

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "host_state.hpp"
+
 namespace rswa {
 
 // Where a request's logical slot i lives: pool row table[base + i] when
@@ -34,29 +36,25 @@ struct RingWriteArgs {
   int32_t n, heads, window, layer;
 };
 
-struct AdvanceArgs {
-  StateArgs st;
-  const int32_t *batch_req;
-  int32_t n;
-};
-
 struct DecodeArgs {
   PoolArgs pool;
   StateArgs st;
-  const int32_t *batch_req;   // [n]
-  const int32_t *split_map;   // [2 * num_splits] (batch entry, split index)
-  const int32_t *split_off;   // [n + 1]
+  const SplitDesc *splits;    // [num_splits]
+  const int32_t *split_off;   // [n + 1] first split of each batch entry
   const void *q;              // [n][H][D]
   void *out;                  // [n][H][D]
   const void *k_new;          // [n][H][D] or null: ring write fused into the split kernel
   const void *v_new;
   float *part_o;              // [num_splits][H][D]
   float2 *part_ml;            // [num_splits][H]  (running max in log2 units, sum)
+  int32_t *merge_cnt;         // [n][H] zero between launches
+  int32_t *step_cnt;          // [n] zero between launches
   const float2 *rope;
   float qscale;               // softmax_scale * log2(e)
   uint32_t layer_bytes;       // bytes of one layer of a pool (< 2^32)
-  int32_t n, heads, window, layer, num_splits, split_tokens;
+  int32_t n, heads, window, layer, num_splits;
   int32_t attention;          // RSWA_ATTENTION_RSWA or RSWA_ATTENTION_SWA
+  int32_t advance;            // nonzero: this launch ends the step (t += 1 per entry)
 };
 
 struct PrefillArgs {
@@ -82,9 +80,9 @@ struct PrefillArgs {
 
 // dtype: RSWA_DTYPE_BF16 or RSWA_DTYPE_F32; head_dim 64 or 128.
 hipError_t launch_ring_write(const RingWriteArgs &a, int dtype, int head_dim, hipStream_t s);
-hipError_t launch_advance(const AdvanceArgs &a, hipStream_t s);
-hipError_t launch_decode_split(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
-hipError_t launch_decode_combine(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
+// Split-KV decode attention with the cross-split merge in the same launch
+// (and, with DecodeArgs::advance, the step's t += 1).
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
 // bf16 MFMA causal prefill attention (query tiles of prefill_mfma_rows() rows).

@@ -254,6 +254,10 @@ int rswa_cache_init(const rswa_config *cfg, void *k_pool, void *v_pool, void *wo
     if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.req_p, 0xff, sizeof(int32_t) * c.max_requests, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.req_t, 0, sizeof(int32_t) * c.max_requests, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.req_base, 0, sizeof(int64_t) * c.max_requests, s);
+    // Merge and step counters start at zero; every decode launch leaves them so.
+    if (e == hipSuccess)
+      e = hipMemsetAsync(h->ws + lay.merge_cnt, 0, sizeof(int32_t) * (size_t)c.max_requests * c.num_heads, s);
+    if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.step_cnt, 0, sizeof(int32_t) * c.max_requests, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return cleanup(e, "uploading the RoPE table");
     // Resolved here, once per device, for rswa_decode_step_fused_noalloc; a
@@ -438,7 +442,7 @@ int rswa_set_batch(rswa_cache *c, int32_t n, const int32_t *req_ids, void *strea
       std::vector<char> blob(bb.bytes, 0);
       put(blob, bb.req, req_ids, n);
       put(blob, bb.split_off, plan.split_off.data(), n + 1);
-      put(blob, bb.split_map, plan.split_map.data(), plan.split_map.size());
+      put(blob, bb.splits, plan.splits.data(), plan.splits.size());
       hipError_t e = c->upload(c->ws + c->lay.batch, blob.data(), bb.bytes, (hipStream_t)stream);
       if (e != hipSuccess) return c->hip_fail(e, "batch upload");
     }
@@ -512,9 +516,12 @@ int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, 
   a.pool = c->pool();
   a.pool.table = c->slot_table;
   a.st = c->state();
-  a.batch_req = (const int32_t *)(dev + bb.req);
-  a.split_map = (const int32_t *)(dev + bb.split_map);
+  a.splits = (const rswa::SplitDesc *)(dev + bb.splits);
   a.split_off = (const int32_t *)(dev + bb.split_off);
+  a.merge_cnt = (int32_t *)(c->ws + c->lay.merge_cnt);
+  a.step_cnt = (int32_t *)(c->ws + c->lay.step_cnt);
+  // The decode that completes the step's layers also advances t on the device.
+  a.advance = c->st.completes_step(layer) ? 1 : 0;
   a.q = q;
   a.out = out;
   a.k_new = k_new;
@@ -535,15 +542,12 @@ int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, 
   a.window = c->cfg.window;
   a.layer = layer;
   a.num_splits = plan.num_splits();
-  a.split_tokens = plan.split_tokens;
   a.attention = c->cfg.attention;
   hipStream_t s = (hipStream_t)stream;
   const int pi = noalloc ? -1 : c->prof_begin(RSWA_KERNEL_DECODE_SPLIT, s);
-  hipError_t e = rswa::launch_decode_split(a, c->cfg.dtype, c->cfg.head_dim, s);
+  hipError_t e = rswa::launch_decode(a, c->cfg.dtype, c->cfg.head_dim, s);
   c->prof_end(RSWA_KERNEL_DECODE_SPLIT, pi, s);
   if (e != hipSuccess) return c->hip_fail(e, "split-KV decode launch");
-  e = rswa::launch_decode_combine(a, c->cfg.dtype, c->cfg.head_dim, s);
-  if (e != hipSuccess) return c->hip_fail(e, "decode combine launch");
   if (fused) c->st.commit_fused(layer);
   else c->st.commit_decode(layer);
   if (capturing(s)) c->st.note_capture();
@@ -578,18 +582,11 @@ int rswa_decode_step_fused_noalloc(rswa_cache *c, int32_t layer, const void *q, 
 int rswa_advance(rswa_cache *c, void *stream) {
   if (!c) return set_global_error(RSWA_E_ARG, "null handle");
   return guarded(c, [&]() -> int {
+    (void)stream;  // the step's last decode kernel already advanced t on the device
     std::string err;
     int rc = c->st.check_advance(&err);
     if (rc != RSWA_OK) return c->fail(rc, err);
-    rswa::BatchBlob bb = rswa::BatchBlob::make((int)c->st.batch().size(), c->st.plan().num_splits());
-    rswa::AdvanceArgs a{};
-    a.st = c->state();
-    a.batch_req = (const int32_t *)(c->ws + c->lay.batch + bb.req);
-    a.n = (int32_t)c->st.batch().size();
-    hipError_t e = rswa::launch_advance(a, (hipStream_t)stream);
-    if (e != hipSuccess) return c->hip_fail(e, "advance launch");
     c->st.commit_advance();
-    if (capturing((hipStream_t)stream)) c->st.note_capture();
     return RSWA_OK;
   });
 }
@@ -626,9 +623,15 @@ int rswa_get_state(rswa_cache *c, int32_t n, const int32_t *req_ids, int32_t *ri
     if (e == hipSuccess)
       e = hipMemcpy(dt.data(), c->ws + c->lay.req_t, sizeof(int32_t) * dt.size(), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return c->hip_fail(e, "reading device state");
+    // Between the step's last decode and rswa_advance the device copy of t
+    // of the batch's requests is already one ahead.
+    const bool ahead = c->st.step_decoded();
+    std::vector<uint8_t> in_batch(cf.max_requests, 0);
+    for (int32_t id : c->st.batch()) in_batch[id] = 1;
     for (int i = 0; i < n; ++i) {
       const rswa::RequestState &r = c->st.request(req_ids[i]);
-      const int32_t p = dp[req_ids[i]], t = dt[req_ids[i]];
+      const int32_t p = dp[req_ids[i]];
+      const int32_t t = dt[req_ids[i]] - ((ahead && in_batch[req_ids[i]]) ? 1 : 0);
       if (p != r.plen || t != r.t)
         return c->fail(RSWA_E_STATE, "device state of request " + std::to_string(req_ids[i]) +
                                          " (P=" + std::to_string(p) + ", t=" + std::to_string(t) +

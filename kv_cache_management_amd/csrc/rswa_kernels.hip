@@ -1,7 +1,8 @@
 // gfx950 kernels of the R-SWA hot path other than decode attention and the
 // MFMA prefill attention: ring write (RoPE at the absolute position, in-place
-// slot overwrite), the step advance, prefill registration and cache write,
-// and a VALU causal prefill attention used for fp32 and as a reference path.
+// slot overwrite), prefill registration and cache write, and a VALU causal
+// prefill attention used for fp32 and as a reference path.  (The step
+// advance, t += 1, runs inside the decode kernel of the step's last layer.)
 //
 // The cache policy is that of page "开源5天Star破万之后：百度Unlimited-OCR的爆火
 // 路径复盘" (www.gtnt.cn/news/146005), section 2.1: prefill rows are kept
@@ -53,12 +54,6 @@ __global__ __launch_bounds__(64) void ring_write_kernel(RingWriteArgs a) {
     V[i] = vn[i];
     V[i + D / 2] = vn[i + D / 2];
   }
-}
-
-// Advance: every active request has one more generated token cached.
-__global__ __launch_bounds__(256) void advance_kernel(AdvanceArgs a) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b < a.n) a.st.t[a.batch_req[b]] += 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -220,12 +215,6 @@ hipError_t launch_ring_write(const RingWriteArgs &a, int dtype, int head_dim, hi
     hipLaunchKernelGGL((ring_write_kernel<T, D>), dim3(a.n * a.heads), dim3(64), 0, s, a);
     return hipGetLastError();
   });
-}
-
-hipError_t launch_advance(const AdvanceArgs &a, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(advance_kernel, dim3((a.n + 255) / 256), dim3(256), 0, s, a);
-  return hipGetLastError();
 }
 
 hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s) {

@@ -92,6 +92,8 @@ static void test_layout() {
       {L.batch, L.batch_bytes},
       {L.part_o, sizeof(float) * c.max_splits * c.num_heads * c.head_dim},
       {L.part_ml, sizeof(float) * 2 * c.max_splits * c.num_heads},
+      {L.merge_cnt, 4u * c.max_requests * c.num_heads},
+      {L.step_cnt, 4u * c.max_requests},
       {L.prefill, L.prefill_bytes}};
   std::sort(rs.begin(), rs.end(), [](R a, R b) { return a.off < b.off; });
   for (size_t i = 0; i < rs.size(); ++i) {
@@ -336,6 +338,31 @@ static void test_prefill_tile_index_limit() {
   CHECK(pp.num_tiles() <= c.max_prefill_blocks());
 }
 
+// Splits of request i tile its key range [key0, P + W) exactly, in order:
+// split_tokens keys each (a multiple of 64), the last one the remainder.
+static void check_tiling(const DecodePlan &p, int n, const int32_t *pl, const int64_t *base,
+                         int window, int32_t (*key0)(int32_t)) {
+  CHECK((int)p.split_off.size() == n + 1 && p.split_off[n] == p.num_splits());
+  int32_t longest = 0;
+  for (int i = 0; i < n; ++i) {
+    int32_t next = key0(pl[i]);
+    for (int j = p.split_off[i]; j < p.split_off[i + 1]; ++j) {
+      const SplitDesc &d = p.splits[j];
+      CHECK(d.b == i && d.p == pl[i] && d.base == base[i]);
+      CHECK(d.k0 == next && d.k1 > d.k0);
+      CHECK(d.k1 - d.k0 == p.split_tokens || j + 1 == p.split_off[i + 1]);
+      CHECK(d.k1 - d.k0 <= p.split_tokens);
+      longest = std::max(longest, d.k1 - d.k0);
+      next = d.k1;
+    }
+    CHECK(next == pl[i] + window);
+  }
+  CHECK(p.split_tokens == longest);
+}
+
+static int32_t rswa_key0(int32_t) { return 0; }
+static int32_t swa_key0(int32_t p) { return std::max(0, p - 127); }
+
 static void test_decode_plan() {
   rswa_config rc = base_cfg();
   rc.max_positions = 32768;
@@ -356,19 +383,35 @@ static void test_decode_plan() {
   }
   register_all(st, 64, ids.data(), pl.data(), base.data());
   DecodePlan p = st.plan_decode(64, ids.data());
-  CHECK(p.split_tokens % 64 == 0 && p.split_tokens >= 64);
-  CHECK((int)p.split_off.size() == 65 && p.split_off[64] == p.num_splits());
-  for (int i = 0; i < 64; ++i) {
-    const int k = p.split_off[i + 1] - p.split_off[i];
-    // splits cover [0, P + W) exactly, the last one non-empty
-    CHECK((int64_t)k * p.split_tokens >= pl[i] + 128);
-    CHECK((int64_t)(k - 1) * p.split_tokens < pl[i] + 128);
-    for (int j = 0; j < k; ++j) {
-      CHECK(p.split_map[2 * (p.split_off[i] + j)] == i);
-      CHECK(p.split_map[2 * (p.split_off[i] + j) + 1] == j);
+  check_tiling(p, 64, pl.data(), base.data(), 128, rswa_key0);
+  for (int j = 0; j < p.num_splits(); ++j) CHECK(p.splits[j].r == ids[p.splits[j].b]);
+  // 64 requests x ~4.4k keys x 10 heads is beyond one round: ~1024-key splits.
+  CHECK(p.split_tokens == kLongSplitKeys);
+  // A batch that fits one round gets the shortest 64-multiple splits that
+  // keep it within kDecodeWaves waves: 8 x 4288 keys x 10 heads -> 384-key
+  // splits, 12 per request (960 waves, 240 blocks).
+  {
+    rswa_config r2 = base_cfg();
+    r2.max_positions = 32768;
+    r2.max_requests = 8;
+    r2.window = 128;
+    r2.num_slots = 8 * 4288;
+    r2.max_prefill_tokens = 1 << 20;
+    HostState s8(resolved(r2));
+    std::vector<int32_t> i8(8), p8(8, 4160);
+    std::vector<int64_t> b8(8);
+    for (int i = 0; i < 8; ++i) {
+      i8[i] = i;
+      b8[i] = (int64_t)i * 4288;
     }
+    register_all(s8, 8, i8.data(), p8.data(), b8.data());
+    DecodePlan q = s8.plan_decode(8, i8.data());
+    check_tiling(q, 8, p8.data(), b8.data(), 128, rswa_key0);
+    CHECK(q.num_splits() * 10 <= kDecodeCUs * kDecodeWavesPerBlock);
+    CHECK(q.split_tokens == 384 && q.split_off[1] == 12);
   }
-  // forced split size; a too-small max_splits is reported
+  // Forced split size: fixed-length splits, the last one shorter; a
+  // too-small max_splits is reported.
   rc.decode_split_tokens = 64;
   rc.max_splits = 100;
   Config c2 = resolved(rc);
@@ -376,6 +419,10 @@ static void test_decode_plan() {
   register_all(st2, 64, ids.data(), pl.data(), base.data());
   std::string err;
   CHECK(st2.check_set_batch(64, ids.data(), &err) == RSWA_E_CAPACITY);
+  DecodePlan p2 = st2.plan_decode(64, ids.data());
+  check_tiling(p2, 64, pl.data(), base.data(), 128, rswa_key0);
+  CHECK(p2.split_tokens == 64);
+  for (int i = 0; i < 64; ++i) CHECK(p2.split_off[i + 1] - p2.split_off[i] == (pl[i] + 128 + 63) / 64);
   rc.decode_split_tokens = 0;
   Config c3 = resolved(rc);
   HostState st3(c3);
@@ -391,6 +438,7 @@ static void test_decode_plan() {
   register_all(st4, 64, ids.data(), pl.data(), base.data());
   CHECK(st4.check_set_batch(64, ids.data(), &err) == RSWA_OK);
   DecodePlan p4 = st4.plan_decode(64, ids.data());
+  check_tiling(p4, 64, pl.data(), base.data(), 128, swa_key0);
   for (int i = 0; i < 64; ++i) {
     CHECK(st4.decode_key0(pl[i]) == pl[i] - 127);
     CHECK(p4.split_off[i + 1] - p4.split_off[i] == (2 * 128 - 1 + 63) / 64);
@@ -404,7 +452,26 @@ static void test_decode_plan() {
   CHECK(resolve_config(bad, &out, &err) == RSWA_E_ARG);
 }
 
-// Chunked prefill: order rules per layer and across layers.
+// The decode of the layer that completes a step advances t on the device.
+static void test_step_completion() {
+  Config c = resolved(base_cfg());  // 2 layers
+  HostState st(c);
+  int32_t ids[1] = {0};
+  int32_t pl[1] = {10};
+  int64_t base[1] = {0};
+  register_all(st, 1, ids, pl, base);
+  st.commit_set_batch(1, ids, st.plan_decode(1, ids));
+  CHECK(!st.step_decoded());
+  CHECK(!st.completes_step(0) && !st.completes_step(1));  // two layers to go
+  st.commit_fused(1);
+  CHECK(st.completes_step(0) && !st.completes_step(1));
+  CHECK(!st.step_decoded());
+  st.commit_fused(0);
+  CHECK(st.step_decoded());
+  st.commit_advance();
+  CHECK(!st.step_decoded() && st.request(0).t == 1);
+}
+
 static void test_chunked_prefill() {
   Config c = resolved(base_cfg());
   HostState st(c);
@@ -495,6 +562,7 @@ int main() {
   test_fused_step();
   test_prefill_tile_index_limit();
   test_decode_plan();
+  test_step_completion();
   test_chunked_prefill();
   test_admission();
   if (g_fail) {

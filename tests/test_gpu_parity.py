@@ -208,6 +208,24 @@ def test_split_size_does_not_change_results(split):
         assert (np.abs(out - out2) <= row_ulp).all(), key
 
 
+@pytest.mark.parametrize("dtype,head_dim,fused", [("bf16", 128, False), ("bf16", 128, True),
+                                                  ("f32", 64, False)])
+def test_merge_of_many_splits(dtype, head_dim, fused):
+    """64-key splits over prefills of 5000, 300 and 2200 keys: 79, 6 and 35
+    splits per (request, head), so the in-kernel merge runs both its
+    one-batch path and its multi-batch path (more than 64 splits, and more
+    splits than one batch of loads holds), every step against the oracle."""
+    w = dataclasses.replace(SMALL_RAGGED, prefill_lens=(5000, 300, 2200), start_steps=(0, 9, 31),
+                            window=32, decode_steps=40, dtype=dtype, head_dim=head_dim,
+                            wid=130 + head_dim + (dtype == "f32") + 2 * fused,
+                            v_std_ratio=1.0 if dtype == "f32" else SMALL_RAGGED.v_std_ratio)
+    sc = H.Scenario(w, steps=w.decode_steps, check_steps=range(w.decode_steps), split_tokens=64,
+                    fused=fused)
+    inputs = H.Inputs(w)
+    res = H.run_gpu(sc, inputs)
+    _check_run(sc, res, inputs, check_pool=False)
+
+
 def test_position_limit_is_reported_and_state_kept():
     from kv_cache_management_amd.rswa import RSWAError, RSWA_E_POSITION
 
