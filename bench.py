@@ -71,7 +71,7 @@ class Job:
     """Device-resident inputs and the cache for one workload."""
 
     def __init__(self, w: W.Workload, decode_steps: int, seed: int = 0, fused: bool = True,
-                 attention: str = "rswa"):
+                 attention: str = "rswa", input_steps: int = 0):
         import torch
         from kv_cache_management_amd import rswa
 
@@ -108,8 +108,11 @@ class Job:
             act = [r for r in range(n) if starts[r] > self.pre - 1 - g]
             self.schedule.append(act)
         g_total = self.pre + decode_steps
-        log(f"allocating decode inputs: {g_total} steps x {L} layers x 3 x {n} x {H} x {D}")
-        self.dec = rnd((g_total, L, 3, n, H, D))
+        # Distinct decode-input steps; step g reads block g mod this (the
+        # launches, and the bytes they read, do not depend on the values).
+        self.input_steps = min(g_total, input_steps) if input_steps > 0 else g_total
+        log(f"allocating decode inputs: {self.input_steps} steps x {L} layers x 3 x {n} x {H} x {D}")
+        self.dec = rnd((self.input_steps, L, 3, n, H, D))
         self.dec_out = torch.empty((L, n, H, D), device=dev, dtype=tdt)
         # raw pointers for the hot loop
         self.ids = np.arange(n, dtype=np.int32)
@@ -170,7 +173,7 @@ class Job:
         lib, h, s = self.lib, self.h, self.sptr
         L = self.w.layers
         for l in range(L):
-            blk = self.dec_ptr0 + ((g * L + l) * 3) * self.row_bytes
+            blk = self.dec_ptr0 + (((g % self.input_steps) * L + l) * 3) * self.row_bytes
             q, k, v = blk, blk + self.row_bytes, blk + 2 * self.row_bytes
             if self.fused:
                 st = lib.rswa_decode_step_fused(h, l, q, k, v, self.out_ptr[l], s)
@@ -242,7 +245,7 @@ class Job:
                 for i in range(k):
                     g = self.pre + i
                     for l in range(L):
-                        blk = self.dec_ptr0 + ((g * L + l) * 3) * self.row_bytes
+                        blk = self.dec_ptr0 + (((g % self.input_steps) * L + l) * 3) * self.row_bytes
                         self._check(lib.rswa_decode_step_fused(
                             h, l, blk, blk + self.row_bytes, blk + 2 * self.row_bytes,
                             self.out_ptr[l], sptr))
@@ -275,11 +278,11 @@ class Job:
         return ms, cnt
 
 
-def traffic_from_profile(workload: str, algorithmic_bytes_per_launch: float):
+def traffic_from_profile(workload: str):
     """HBM traffic per decode launch from the committed PMC summary of this
-    workload: (bytes, record) when it was taken on the current kernel source
-    and on launches with the same algorithmic bytes as this line's (the same
-    steps of the same workload), else (None, reason)."""
+    workload, taken on the current kernel source: the record (HBM bytes per
+    launch of the profiled launches, their own algorithmic bytes and the
+    ratio), or (None, reason)."""
     path = os.path.join(PROFILE_DIR, f"decode_split_{workload}_pmc.md")
     if not os.path.exists(path):
         return None, f"no {os.path.basename(path)}"
@@ -293,10 +296,7 @@ def traffic_from_profile(workload: str, algorithmic_bytes_per_launch: float):
         return None, "no traffic record"
     if rec.get("kernel_source_sha256_16") != kernel_source_sha("decode_split"):
         return None, "decode kernel changed since the counters were taken"
-    alg = rec.get("algorithmic_bytes_per_launch", 0)
-    if abs(alg - algorithmic_bytes_per_launch) > 1e-6 * algorithmic_bytes_per_launch:
-        return None, "counters were taken on other launches (different algorithmic bytes)"
-    return rec.get("hbm_bytes_per_launch"), rec
+    return rec, None
 
 
 def measured_peaks(torch, rswa, read_gib: int = 4):
@@ -635,6 +635,9 @@ def main():
     ap.add_argument("--workload", default="ragged_mix", choices=sorted(W.ALL))
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="measured decode steps per job (default: the workload's)")
+    ap.add_argument("--input-steps", type=int, default=0,
+                    help="distinct decode-input steps, cycled (default: one per step); for "
+                         "profiler runs that cannot hold the full input set")
     ap.add_argument("--unfused", action="store_true",
                     help="separate rswa_ring_write + rswa_decode_step calls instead of "
                          "rswa_decode_step_fused")
@@ -702,7 +705,7 @@ def main():
         w = dataclasses.replace(w, window=args.window)
     log(f"workload {w.name}: {w.batch} requests x {w.layers} layers, sum P = {sum(w.prefill_lens)}, "
         f"{steps} decode steps")
-    job = Job(w, steps, fused=not args.unfused, attention=args.attention)
+    job = Job(w, steps, fused=not args.unfused, attention=args.attention, input_steps=args.input_steps)
     if args.graph:
         if args.unfused or args.cold:
             sys.exit("--graph captures fused steps with warm caches only")
@@ -764,12 +767,19 @@ def main():
         per_launch_bytes = job.kv_bytes / job.kv_launches
         avg_s = k_dec[0] / k_dec[1] / 1e3
         achieved = per_launch_bytes / avg_s / 1e9
-        traffic, trec = traffic_from_profile(w.name, per_launch_bytes)
+        trec, why = traffic_from_profile(w.name)
+        # The PMC record is paired with the algorithmic bytes of the launches
+        # it profiled (a shorter run of this workload), never with this line's.
         roofline = {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": traffic,
-                    "traffic_over_algorithmic": (round(traffic / per_launch_bytes, 4) if traffic else None),
-                    "traffic_note": (f"profiles/decode_split_{w.name}_pmc.md" if traffic else trec),
+                    "traffic": trec["hbm_bytes_per_launch"] if trec else None,
+                    "traffic_algorithmic_bytes_per_launch":
+                        trec["algorithmic_bytes_per_launch"] if trec else None,
+                    "traffic_over_algorithmic": (round(trec["hbm_bytes_per_launch"] /
+                                                       trec["algorithmic_bytes_per_launch"], 4)
+                                                 if trec else None),
+                    "traffic_note": (f"profiles/decode_split_{w.name}_pmc.md: {trec['launches_note']}"
+                                     if trec else why),
                     "algorithmic_bytes_per_launch": int(per_launch_bytes),
                     "avg_launch_us": round(avg_s * 1e6, 2), "launches": k_dec[1],
                     "timing": "HIP event pair per launch, in a separate job after the timed steps"}
@@ -798,6 +808,7 @@ def main():
                    "head_dim": w.head_dim, "window": w.window, "decode_steps": steps,
                    "prefill_tokens": sum(w.prefill_lens),
                    "kv_layout": "page-size-1 slot table" if w.paged else "contiguous",
+                   "decode_input_steps": job.input_steps,
                    "decode_call": "rswa_ring_write + rswa_decode_step" if args.unfused
                    else (f"rswa_decode_step_fused, replayed as a graph of {args.graph} steps"
                          if args.graph else "rswa_decode_step_fused"),
@@ -805,6 +816,7 @@ def main():
                    else ("R-SWA" if w.window < steps + max(w.starts()) else
                          "growing full cache (W >= generated tokens)")},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "decode_algorithmic_bytes_per_launch": int(job.kv_bytes / job.kv_launches),
         "decode_steps_per_s": round(steps * args.steps / dec_s, 2),
         "decode_ms_per_step": round(dec_s * 1e3 / (steps * args.steps), 4),
         "prefill_tflops": round(pf_tflops, 2),

@@ -24,36 +24,51 @@ namespace {
 using namespace dev;
 
 // ---------------------------------------------------------------------------
-// Ring write: one block of 64 threads per (batch entry, head).
-// slot = P + (t mod W), position = P + t; K row = RoPE(k_new, P + t), V row =
-// v_new.  Thread i handles the rotation pair (i, i + D/2).
+// Ring write: TPP = (D/2) / EPL threads per (batch entry, head), 64 threads
+// per block.  slot = P + (t mod W), position = P + t; K row = RoPE(k_new,
+// P + t), V row = v_new.  Thread c moves 16-byte pieces: elements
+// [c*EPL, c*EPL + EPL) of the lower half and the same offsets of the upper
+// half (their rotation partners) of k and v.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(64) void ring_write_kernel(RingWriteArgs a) {
-  const int b = blockIdx.x / a.heads;
-  const int h = blockIdx.x % a.heads;
+  constexpr int EPL = 16 / (int)sizeof(T);
+  constexpr int TPP = (D / 2) / EPL;
+  const int64_t gid = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int64_t pair = gid / TPP;
+  if (pair >= (int64_t)a.n * a.heads) return;
+  const int c = (int)(gid % TPP);
+  const int b = (int)(pair / a.heads);
+  const int h = (int)(pair % a.heads);
   const int r = a.batch_req[b];
   const int p_len = a.st.plen[r];
   const int t = a.st.t[r];
   const int pos = p_len + t;
   const int slot = p_len + t % a.window;
   const int64_t row = pool_row(a.pool.table, a.st.base[r], slot);
-  const int64_t dst = (int64_t)a.layer * a.pool.layer_stride + (row * a.heads + h) * D;
-  const int64_t src = ((int64_t)b * a.heads + h) * D;
-  const T *kn = (const T *)a.k_new + src;
-  const T *vn = (const T *)a.v_new + src;
+  const int64_t dst = (int64_t)a.layer * a.pool.layer_stride + (row * a.heads + h) * D + c * EPL;
+  const int64_t src = ((int64_t)b * a.heads + h) * D + c * EPL;
+  const uint4 k1 = *(const uint4 *)((const T *)a.k_new + src);
+  const uint4 k2 = *(const uint4 *)((const T *)a.k_new + src + D / 2);
+  const uint4 v1 = *(const uint4 *)((const T *)a.v_new + src);
+  const uint4 v2 = *(const uint4 *)((const T *)a.v_new + src + D / 2);
+  float x1[EPL], x2[EPL];
+  Vec16<T>::unpack(k1, x1);
+  Vec16<T>::unpack(k2, x2);
+  const float2 *cs = a.rope + (int64_t)pos * (D / 2) + c * EPL;
+  T r1[EPL], r2[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const float2 cc = cs[e];
+    r1[e] = from_f<T>(rope_lo(x1[e], x2[e], cc));
+    r2[e] = from_f<T>(rope_hi(x1[e], x2[e], cc));
+  }
   T *K = (T *)a.pool.k + dst;
   T *V = (T *)a.pool.v + dst;
-  const float2 *cs = a.rope + (int64_t)pos * (D / 2);
-  for (int i = threadIdx.x; i < D / 2; i += 64) {
-    const float2 c = cs[i];
-    const float x1 = to_f(kn[i]);
-    const float x2 = to_f(kn[i + D / 2]);
-    K[i] = from_f<T>(rope_lo(x1, x2, c));
-    K[i + D / 2] = from_f<T>(rope_hi(x1, x2, c));
-    V[i] = vn[i];
-    V[i + D / 2] = vn[i + D / 2];
-  }
+  *(uint4 *)K = __builtin_bit_cast(uint4, r1);
+  *(uint4 *)(K + D / 2) = __builtin_bit_cast(uint4, r2);
+  *(uint4 *)V = v1;
+  *(uint4 *)(V + D / 2) = v2;
 }
 
 // ---------------------------------------------------------------------------
@@ -122,14 +137,21 @@ __global__ __launch_bounds__(256) void prefill_cache_write_kernel(PrefillArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Causal prefill attention on the VALU (fp32 path and cross-check path).
-// One block of 64 threads per (query tile of 64 rows, head); thread = query
-// row.  Keys (already rotated, read from the pool) and values are staged 32
-// at a time in LDS; softmax is online in base 2.
+// Causal prefill attention on the VALU (the fp32 path).  One block of 256
+// threads per (query tile of 64 rows, head); LPQ = 4 lanes per query row,
+// each holding E = D / 4 elements of the rotated query and of the output
+// (element j * E + e in lane j of the row), so no thread keeps a whole head
+// vector.  Keys (already rotated, read from the pool) and values are staged
+// KT at a time in LDS, element j * E + e of a row at position e * LPQ + j so
+// the four lanes of a row read four consecutive words.  A key's score is the
+// lanes' partial dot products summed over the row's four lanes; softmax is
+// online in base 2.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(64) void prefill_attn_valu_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_attn_valu_kernel(PrefillArgs a) {
   constexpr int KT = 32;
+  constexpr int LPQ = 4;
+  constexpr int E = D / LPQ;
   __shared__ float ks[KT][D];
   __shared__ float vs[KT][D];
   const int b = a.tiles[2 * blockIdx.x];
@@ -141,50 +163,63 @@ __global__ __launch_bounds__(64) void prefill_attn_valu_kernel(PrefillArgs a) {
   const int q_off = a.qoff[b];   // position of its first row
   const int64_t base = a.base[b];
   const int64_t cu = a.cu[b];
-  const int li = qt * 64 + threadIdx.x;   // row in the chunk
-  const int i = q_off + li;               // its position
+  const int tid = threadIdx.x;
+  const int j = tid % LPQ;                 // this lane's element slice
+  const int li = qt * 64 + tid / LPQ;      // row in the chunk
+  const int i = q_off + li;                // its position
   const bool active = li < c_len;
   const int64_t layer0 = (int64_t)a.layer * a.pool.layer_stride;
 
-  float qh[D];
-  float o[D];
+  // Rotated query slice: element d = j * E + e pairs with d +- D/2.
+  float qh[E];
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    qh[e] = 0.f;
+    o[e] = 0.f;
+  }
   if (active) {
     const T *qp = (const T *)a.q + ((cu + li) * a.heads + h) * D;
     const float2 *cs = a.rope + (int64_t)i * (D / 2);
-    for (int d = 0; d < D / 2; ++d) {
-      const float2 c = cs[d];
-      const float x1 = to_f(qp[d]);
-      const float x2 = to_f(qp[d + D / 2]);
-      qh[d] = (x1 * c.x - x2 * c.y) * a.qscale;
-      qh[d + D / 2] = (x2 * c.x + x1 * c.y) * a.qscale;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int d = j * E + e;
+      const float2 c = cs[d % (D / 2)];
+      const float x = to_f(qp[d]);
+      const float y = d < D / 2 ? -to_f(qp[d + D / 2]) : to_f(qp[d - D / 2]);
+      qh[e] = (x * c.x + y * c.y) * a.qscale;
     }
   }
-  for (int d = 0; d < D; ++d) o[d] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const int kend = q_off + min(c_len, (qt + 1) * 64);
+  const int last = q_off + min(c_len, (qt + 1) * 64) - 1;  // the tile's last row position
   for (int k0 = 0; k0 < kend; k0 += KT) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < KT * D; idx += 64) {
+    for (int idx = tid; idx < KT * D; idx += 256) {
       const int kk = idx / D;
       const int d = idx % D;
-      const int j = k0 + kk;
-      if (j < kend) {
-        const int64_t off = layer0 + (pool_row(a.pool.table, base, j) * a.heads + h) * D + d;
-        ks[kk][d] = to_f(((const T *)a.pool.k)[off]);
-        vs[kk][d] = to_f(((const T *)a.pool.v)[off]);
+      const int jj = k0 + kk;
+      if (jj < kend) {
+        const int64_t off = layer0 + (pool_row(a.pool.table, base, jj) * a.heads + h) * D + d;
+        ks[kk][(d % E) * LPQ + d / E] = to_f(((const T *)a.pool.k)[off]);
+        vs[kk][(d % E) * LPQ + d / E] = to_f(((const T *)a.pool.v)[off]);
       }
     }
     __syncthreads();
-    if (active) {
-      const int jn = min(KT, i - k0 + 1);
-      for (int kk = 0; kk < jn; ++kk) {
-        float s = 0.f;
-        for (int d = 0; d < D; ++d) s = fmaf(qh[d], ks[kk][d], s);
+    const int nk = min(KT, min(kend, last + 1) - k0);  // keys of this tile any row may see
+    for (int kk = 0; kk < nk; ++kk) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part = fmaf(qh[e], ks[kk][e * LPQ + j], part);
+      part += __shfl_xor(part, 1);  // sum over the row's four lanes
+      const float s = part + __shfl_xor(part, 2);
+      if (active && k0 + kk <= i) {
         const float m_new = fmaxf(m_run, s);
         const float alpha = exp2f(m_run - m_new);
         const float p = exp2f(s - m_new);
         l_run = l_run * alpha + p;
-        for (int d = 0; d < D; ++d) o[d] = fmaf(p, vs[kk][d], o[d] * alpha);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = fmaf(p, vs[kk][e * LPQ + j], o[e] * alpha);
         m_run = m_new;
       }
     }
@@ -192,7 +227,8 @@ __global__ __launch_bounds__(64) void prefill_attn_valu_kernel(PrefillArgs a) {
   if (active) {
     T *op = (T *)a.out + ((cu + li) * a.heads + h) * D;
     const float inv = 1.f / l_run;
-    for (int d = 0; d < D; ++d) op[d] = from_f<T>(o[d] * inv);
+#pragma unroll
+    for (int e = 0; e < E; ++e) op[j * E + e] = from_f<T>(o[e] * inv);
   }
 }
 
@@ -212,7 +248,9 @@ hipError_t launch_ring_write(const RingWriteArgs &a, int dtype, int head_dim, hi
   return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
     using T = decltype(tv);
     constexpr int D = decltype(dv)::value;
-    hipLaunchKernelGGL((ring_write_kernel<T, D>), dim3(a.n * a.heads), dim3(64), 0, s, a);
+    constexpr int TPP = (D / 2) / (16 / (int)sizeof(T));
+    const int64_t threads = (int64_t)a.n * a.heads * TPP;
+    hipLaunchKernelGGL((ring_write_kernel<T, D>), dim3((unsigned)((threads + 63) / 64)), dim3(64), 0, s, a);
     return hipGetLastError();
   });
 }
@@ -246,7 +284,7 @@ hipError_t launch_prefill_attention(const PrefillArgs &a, int dtype, int head_di
   return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
     using T = decltype(tv);
     constexpr int D = decltype(dv)::value;
-    hipLaunchKernelGGL((prefill_attn_valu_kernel<T, D>), dim3(a.num_tiles), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn_valu_kernel<T, D>), dim3(a.num_tiles), dim3(256), 0, s, a);
     return hipGetLastError();
   });
 }

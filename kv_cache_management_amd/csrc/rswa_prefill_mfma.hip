@@ -146,8 +146,10 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   }
 
   // ---- queries: B operand fragments, rotated at their positions ----------
+  // (loaded once the first key/value tiles are requested, so both latencies
+  // overlap)
   bf16x8 qf[KS];
-  {
+  auto load_queries = [&]() {
     float qv[KS][8];
     const bool qok = li < c_len;
     const bf16 *qp = (const bf16 *)a.q + ((cu + (qok ? li : 0)) * a.heads + h) * D;
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
         qf[ks + KS / 2][e] = (bf16)(x2 * c.x + x1 * c.y);
       }
     }
-  }
+  };
 
   f32x16 o[DB];
 #pragma unroll
@@ -376,6 +378,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void prefill_mfma_kernel(Pref
   dma(rv, lv0, 0, rows_k);
   dma(rk, lk1, kBN, rows_v);
   fetch_rows(rows_k, 2 * kBN);
+  load_queries();
   lds_publish_barrier();
 
   // A wave with no valid query row (the tail of a chunk's last query tile)

@@ -92,7 +92,7 @@ def _pmc_rows(d: str, counter: str, kernel: str):
 
 
 def pmc_summary(fetch: str, write: str, copy_fetch: str, copy_write: str, kernel: str, last: int,
-                algorithmic: float, command: str) -> str:
+                algorithmic: float, command: str, launches_note: str = "") -> str:
     cf = _pmc_rows(copy_fetch, "FETCH_SIZE", "")
     cw = _pmc_rows(copy_write, "WRITE_SIZE", "")
     # the copy kernel: the dispatches that moved about 1 GiB
@@ -110,7 +110,8 @@ def pmc_summary(fetch: str, write: str, copy_fetch: str, copy_write: str, kernel
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "hbm_fetch_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
            "hbm_bytes_per_launch": int(fetch_b + write_b),
-           "algorithmic_bytes_per_launch": int(algorithmic), "launches_averaged": len(f_tail)}
+           "algorithmic_bytes_per_launch": int(algorithmic), "launches_averaged": len(f_tail),
+           "launches_note": launches_note or f"last {len(f_tail)} dispatches of the profiled run"}
     lines = [f"# rocprofv3 PMC: HBM traffic of {kernel}", "", "Commands:", "", "```", command, "```", "",
              f"Copy calibration (1 GiB read + 1 GiB written by one copy kernel): FETCH_SIZE reads "
              f"{1 / f_scale:.3f}x and WRITE_SIZE {1 / w_scale:.3f}x the true bytes, so they are scaled by "
@@ -144,13 +145,15 @@ def main(argv=None):
     p.add_argument("--last", type=int, default=0)
     p.add_argument("--algorithmic-bytes", type=float, required=True)
     p.add_argument("--command", required=True)
+    p.add_argument("--launches-note", default="",
+                   help="which launches were averaged (recorded beside the traffic)")
     p.add_argument("--out")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         text = trace_summary(a.dir, a.kernel, a.last, a.command, a.max_grid)
     else:
         text = pmc_summary(a.fetch, a.write, a.copy_fetch, a.copy_write, a.kernel, a.last,
-                           a.algorithmic_bytes, a.command)
+                           a.algorithmic_bytes, a.command, a.launches_note)
     if a.out:
         open(a.out, "w").write(text)
     else:
