@@ -6,6 +6,7 @@
         --copy-fetch DIR --copy-write DIR --kernel decode_split --last N \
         --algorithmic-bytes B --command "..." [--out FILE]
 
+`counters` sums the counters of `--pmc` runs over a kernel's last dispatches.
 `trace` reads a `--kernel-trace --stats --output-format csv` directory and
 reports rocprofv3's own per-kernel statistics plus the mean duration of the
 last N dispatches of one kernel (the measured steps of a benchmark run come
@@ -126,6 +127,32 @@ def pmc_summary(fetch: str, write: str, copy_fetch: str, copy_write: str, kernel
     return "\n".join(lines)
 
 
+def counters_summary(dirs, kernel: str, last: int, command: str) -> str:
+    """Sums of every counter over the last `last` dispatches of `kernel` in
+    each --pmc run directory, plus the ratios used to read them."""
+    vals = {}
+    for d in dirs:
+        rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+        rows = [r for r in rows if kernel in r.get("Kernel_Name", "")]
+        ids = sorted({int(r["Dispatch_Id"]) for r in rows})
+        keep = set(ids[-last:] if last else ids)
+        for r in rows:
+            if int(r["Dispatch_Id"]) in keep:
+                vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = [command, f"({kernel}: sums over the last {last or 'all'} dispatch(es) of each run)", ""]
+    lines += [f"{k} {int(v)}" for k, v in sorted(vals.items())]
+    wave = vals.get("SQ_WAVE_CYCLES")
+    if wave:
+        for k in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS"):
+            if k in vals:
+                lines.append(f"{k} / SQ_WAVE_CYCLES = {vals[k] / wave:.3f}")
+    if "SQ_INSTS_MFMA" in vals and "SQ_INSTS_VALU" in vals:
+        lines.append(f"(SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA = "
+                     f"{(vals['SQ_INSTS_VALU'] - vals['SQ_INSTS_MFMA']) / vals['SQ_INSTS_MFMA']:.2f}")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -148,9 +175,17 @@ def main(argv=None):
     p.add_argument("--launches-note", default="",
                    help="which launches were averaged (recorded beside the traffic)")
     p.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--last", type=int, default=1)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         text = trace_summary(a.dir, a.kernel, a.last, a.command, a.max_grid)
+    elif a.cmd == "counters":
+        text = counters_summary(a.dirs, a.kernel, a.last, a.command)
     else:
         text = pmc_summary(a.fetch, a.write, a.copy_fetch, a.copy_write, a.kernel, a.last,
                            a.algorithmic_bytes, a.command, a.launches_note)

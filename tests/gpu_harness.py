@@ -26,6 +26,23 @@ def tolerances(dtype: str):
     return (BF16_ABS, BF16_ROW_REL) if dtype == "bf16" else (F32_ABS, F32_ROW_REL)
 
 
+# Observed error maxima per (test, kind of output, dtype): written by the
+# session hook in conftest.py when RSWA_PARITY_LOG names a file.
+ERROR_LOG: Dict[tuple, dict] = {}
+
+
+def _log_error(what: str, dtype: str, max_abs: float, max_rel: float, rows: int):
+    import os
+
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    key = (test, (what.split(" ") or ["?"])[0], dtype)
+    rec = ERROR_LOG.setdefault(key, {"max_abs": 0.0, "max_row_rel": 0.0, "rows": 0, "checks": 0})
+    rec["max_abs"] = max(rec["max_abs"], max_abs)
+    rec["max_row_rel"] = max(rec["max_row_rel"], max_rel)
+    rec["rows"] += rows
+    rec["checks"] += 1
+
+
 def compare(got: np.ndarray, want: np.ndarray, dtype: str, what: str = ""):
     """max |g - o| <= abs_tol and, per output row (last axis), max|g - o| / max|o| <= rel_tol."""
     abs_tol, rel_tol = tolerances(dtype)
@@ -38,6 +55,7 @@ def compare(got: np.ndarray, want: np.ndarray, dtype: str, what: str = ""):
     denom = np.abs(want).max(axis=-1)
     row_rel = err.max(axis=-1) / np.maximum(denom, 1e-30)
     max_rel = float(row_rel.max()) if row_rel.size else 0.0
+    _log_error(what, dtype, max_abs, max_rel, int(row_rel.size))
     assert max_abs <= abs_tol, f"{what}: max abs err {max_abs:.3e} > {abs_tol}"
     assert max_rel <= rel_tol, f"{what}: max row-relative err {max_rel:.3e} > {rel_tol}"
     return max_abs, max_rel
