@@ -370,6 +370,7 @@ DecodePlan HostState::plan_decode(int32_t n, const int32_t *ids) const {
       while (splits_of(sz) * heads > kDecodeWaves) sz += kSplitQuantum;
     } else {
       sz = kLongSplitKeys;
+      while (splits_of(sz) * heads > resident_waves_ && sz < longest) sz += kSplitQuantum;
     }
     while (splits_of(sz) > cfg_.max_splits) sz += kSplitQuantum;
   }

@@ -29,12 +29,18 @@ constexpr int kSplitQuantum = 64;      // forced split sizes are multiples of th
 // slower).  Batches of at most kOneRoundKeys key-heads run as one round of
 // at most kDecodeWaves waves (one per SIMD, blocks of four, at most one
 // block per CU), with the shortest split length that fits; larger batches use
-// kLongSplitKeys-key splits.
+// kLongSplitKeys-key splits, lengthened until every wave of the launch is
+// resident at once: blocks that do not fit start only when others finish
+// and then stream alone, at the end of the step.
 constexpr int kDecodeWaves = 1024;          // 256 CUs x 4 SIMDs
 constexpr int kDecodeWavesPerBlock = 4;
 constexpr int kDecodeCUs = 256;
 constexpr int kLongSplitKeys = 1024;
 constexpr int64_t kOneRoundKeys = (int64_t)kDecodeWaves * 1280;
+// Decode waves the GPU holds at once when the device was not asked (three
+// per SIMD: the kernel's register count); rswa_cache_init sets the measured
+// figure.
+constexpr int64_t kDefaultResidentWaves = 3 * (int64_t)kDecodeWaves;
 constexpr int kDefaultMaxPositions = 32768;
 constexpr int64_t kDefaultMaxPrefillTokens = 262144;
 constexpr int kPrefillTileMin = 64;    // smallest prefill query tile of any kernel
@@ -187,6 +193,9 @@ class HostState {
 
   int check_set_batch(int32_t n, const int32_t *ids, std::string *err) const;
   DecodePlan plan_decode(int32_t n, const int32_t *ids) const;
+  // Decode waves the device keeps resident at once (> 0).
+  void set_resident_waves(int64_t w) { resident_waves_ = w > 0 ? w : kDefaultResidentWaves; }
+  int64_t resident_waves() const { return resident_waves_; }
   void commit_set_batch(int32_t n, const int32_t *ids, DecodePlan plan);
 
   int check_ring_write(int32_t layer, std::string *err) const;
@@ -237,6 +246,7 @@ class HostState {
   std::vector<int32_t> batch_;
   DecodePlan plan_;
   std::vector<uint8_t> written_, decoded_;
+  int64_t resident_waves_ = kDefaultResidentWaves;
   uint64_t epoch_ = 0;           // committed rswa_set_batch calls
   int64_t captured_epoch_ = -1;  // epoch of the last captured decode work
 };

@@ -83,6 +83,9 @@ hipError_t launch_ring_write(const RingWriteArgs &a, int dtype, int head_dim, hi
 // Split-KV decode attention with the cross-split merge in the same launch
 // (and, with DecodeArgs::advance, the step's t += 1).
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t s);
+// Decode waves the current device keeps resident at once for (dtype,
+// head_dim): the fewest over the kernel's layout / fused variants.
+hipError_t decode_resident_waves(int dtype, int head_dim, int64_t *waves);
 hipError_t launch_prefill_register(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_cache_write(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
 // bf16 MFMA causal prefill attention (query tiles of prefill_mfma_rows() rows).

@@ -260,6 +260,13 @@ int rswa_cache_init(const rswa_config *cfg, void *k_pool, void *v_pool, void *wo
     if (e == hipSuccess) e = hipMemsetAsync(h->ws + lay.step_cnt, 0, sizeof(int32_t) * c.max_requests, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return cleanup(e, "uploading the RoPE table");
+    // How many decode waves fit on the device at once bounds the split
+    // count the planner picks (a failed query keeps the built-in figure).
+    int64_t resident = 0;
+    if (rswa::decode_resident_waves(c.dtype, c.head_dim, &resident) == hipSuccess && resident > 0)
+      h->st.set_resident_waves(resident);
+    else
+      (void)hipGetLastError();
     // Resolved here, once per device, for rswa_decode_step_fused_noalloc; a
     // failure only disables that entry point.
     e = rswa::noalloc_scratch_address(&h->noalloc_scratch);

@@ -9,6 +9,7 @@
 // of the slots, so decode reads logical slots 0 .. L-1 in slot order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "device_common.hpp"
@@ -498,6 +499,30 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream
     else
       hipLaunchKernelGGL((decode_split_kernel<T, D, false, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
+  });
+}
+
+hipError_t decode_resident_waves(int dtype, int head_dim, int64_t *waves) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  return dispatch(dtype, head_dim, [&](auto tv, auto dv) {
+    using T = decltype(tv);
+    constexpr int D = decltype(dv)::value;
+    const void *k[4] = {(const void *)decode_split_kernel<T, D, true, true>,
+                        (const void *)decode_split_kernel<T, D, true, false>,
+                        (const void *)decode_split_kernel<T, D, false, true>,
+                        (const void *)decode_split_kernel<T, D, false, false>};
+    int fewest = 1 << 30;
+    for (const void *f : k) {
+      int blocks = 0;
+      const hipError_t r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, f, 256, 0);
+      if (r != hipSuccess) return r;
+      fewest = std::min(fewest, blocks);
+    }
+    *waves = (int64_t)fewest * 4 * cus;
+    return hipSuccess;
   });
 }
 

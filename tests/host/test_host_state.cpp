@@ -385,8 +385,22 @@ static void test_decode_plan() {
   DecodePlan p = st.plan_decode(64, ids.data());
   check_tiling(p, 64, pl.data(), base.data(), 128, rswa_key0);
   for (int j = 0; j < p.num_splits(); ++j) CHECK(p.splits[j].r == ids[p.splits[j].b]);
-  // 64 requests x ~4.4k keys x 10 heads is beyond one round: ~1024-key splits.
-  CHECK(p.split_tokens == kLongSplitKeys);
+  // 64 requests x ~4.4k keys x 10 heads is beyond one round: 1024-key
+  // splits, lengthened (in 64-key steps) until every wave is resident at once.
+  CHECK(st.resident_waves() == kDefaultResidentWaves);
+  CHECK(p.split_tokens > kLongSplitKeys && p.split_tokens % kSplitQuantum == 0);
+  CHECK(p.num_splits() * 10 <= st.resident_waves());
+  {
+    // one 64-key step shorter would not fit
+    int64_t k = 0;
+    for (int i = 0; i < 64; ++i) k += (pl[i] + 128 + p.split_tokens - 65) / (p.split_tokens - 64);
+    CHECK(k * 10 > st.resident_waves());
+  }
+  // With room for every 1024-key split's wave the split stays at 1024 keys.
+  st.set_resident_waves(int64_t(1) << 20);
+  CHECK(st.plan_decode(64, ids.data()).split_tokens == kLongSplitKeys);
+  st.set_resident_waves(0);  // back to the built-in figure
+  CHECK(st.resident_waves() == kDefaultResidentWaves);
   // A batch that fits one round gets the shortest 64-multiple splits that
   // keep it within kDecodeWaves waves: 8 x 4288 keys x 10 heads -> 384-key
   // splits, 12 per request (960 waves, 240 blocks).
