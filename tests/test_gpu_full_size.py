@@ -90,3 +90,34 @@ def test_doc100_chunked_prefill_full_size():
                 H.compare(got[b * ln:(b + 1) * ln][rows], want, w.dtype, f"chunk {s0} layer {l} req {r}")
     _decode_and_check(cache, w, inputs, ids, 3, {r: 0 for r in ids})
     cache.close()
+
+
+def test_longest_context_full_size():
+    """A request whose prefill and decode fill the whole RoPE table (page
+    "开源5天Star破万之后：百度Unlimited-OCR的爆火路径复盘", section 2.1: the
+    32768-position context of config.json): its last step writes and attends
+    at position 32767, in the paged layout beside a short request; the step
+    after it is refused with the state kept."""
+    from kv_cache_management_amd.rswa import RSWAError, RSWA_E_POSITION
+    import torch
+
+    steps = 400
+    long_p = W.MAX_POSITIONS - steps
+    w = W.Workload(400, "longest_context", layers=1, heads=10, head_dim=128, dtype="bf16",
+                   prefill_lens=(long_p, W.TOKENS_PER_PAGE + 16), window=W.WINDOW,
+                   decode_steps=steps, input_std=1.0 / np.sqrt(128.0), paged=True)
+    check = sorted(set(H.sampled_steps(steps, w.window)) | {steps - 2})
+    sc = H.Scenario(w, steps=steps, check_steps=check,
+                    prefill_rows=lambda p: H.sampled_rows(p, w.wid), poison=True)
+    inputs = H.Inputs(w)
+    res = H.run_gpu(sc, inputs)
+    _check_run(sc, res, inputs)
+    cache = res["cache"]
+    rp, cl, npos = cache.get_state([0, 1])
+    assert list(npos) == [W.MAX_POSITIONS, W.TOKENS_PER_PAGE + 16 + steps]
+    assert list(cl) == [long_p + w.window, W.TOKENS_PER_PAGE + 16 + w.window]
+    z = torch.zeros((2, w.heads, w.head_dim), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(RSWAError) as e:
+        cache.ring_write(0, z, z)
+    assert e.value.status == RSWA_E_POSITION
+    assert [list(x) for x in cache.get_state([0, 1])] == [list(rp), list(cl), list(npos)]
