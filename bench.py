@@ -385,6 +385,94 @@ def prefill_main(runs: int = 3):
             "avg_launch_us": round(avg_s * 1e6, 1), "launches": cnt}
 
 
+def power_clock(torch, rswa, secs: float = 6.0):
+    """Socket power and graphics clock while one load runs back to back:
+    idle, the 100-page prefill (4 x 25728 tokens, one layer), the MFMA-only
+    loop on zero and then on random bf16 operands, the streaming read.
+    amd-smi is sampled from a thread (`amd-smi metric -p -c --json`, about
+    every 0.1 s) and each phase reports the median of its samples.  It shows
+    which figures the board's power limit holds down: the matrix cores on
+    random operands run at the power cap with the clock lowered, while zero
+    operands and HBM streaming keep the full clock."""
+    import statistics
+    import subprocess
+    import threading
+    import time
+
+    cmd = ["amd-smi", "metric", "-p", "-c", "--json"]
+    dev = torch.device("cuda", torch.cuda.current_device())
+    stream = torch.cuda.current_stream(dev)
+
+    def sample():
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        try:
+            j = json.loads(r.stdout)
+            g = j["gpu_data"][0] if isinstance(j, dict) else j[0]
+            watts = float(g["power"]["socket_power"]["value"])
+            clks = [v["clk"]["value"] for k, v in g["clock"].items()
+                    if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+            return watts, statistics.mean(clks)
+        except (ValueError, KeyError, IndexError, TypeError):
+            return None
+
+    if sample() is None:
+        return {"error": "amd-smi gave no power / clock reading", "sampler": " ".join(cmd)}
+    job = Job(W.DOC100, 1)
+    job.run()
+    sink = torch.empty(rswa.RSWA_MEASURE_SINK_WORDS, dtype=torch.int32, device=dev)
+    ops = {k: (torch.randn if k == "random" else torch.zeros)(
+        (rswa.RSWA_MEASURE_MFMA_FRAGMENTS, 8), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        for k in ("random", "zeros")}
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev).fill_(7)
+    torch.cuda.synchronize()
+    samples, stop = [], [False]
+
+    def poll():
+        while not stop[0]:
+            t0 = time.time()
+            v = sample()
+            if v:
+                samples.append((t0, time.time(), v))
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    loads = [
+        ("idle", lambda: time.sleep(0.05)),
+        ("prefill_doc100", lambda: job.run()),
+        ("idle", lambda: time.sleep(0.05)),
+        ("mfma_zeros", lambda: rswa.rswa_measure_mfma(ops["zeros"].data_ptr(), 1_500_000, sink.data_ptr(),
+                                                      stream.cuda_stream)),
+        ("idle", lambda: time.sleep(0.05)),
+        ("mfma_random", lambda: rswa.rswa_measure_mfma(ops["random"].data_ptr(), 1_500_000,
+                                                       sink.data_ptr(), stream.cuda_stream)),
+        ("idle", lambda: time.sleep(0.05)),
+        ("hbm_read", lambda: rswa.rswa_measure_read(buf.data_ptr(), buf.numel(), sink.data_ptr(),
+                                                    stream.cuda_stream)),
+    ]
+    phases = []
+    for name, fn in loads:
+        log(f"power: {name}")
+        t0, calls = time.time(), 0
+        while time.time() - t0 < (secs / 2 if name == "idle" else secs):
+            fn()
+            torch.cuda.synchronize()
+            calls += 1
+        phases.append((name, t0, time.time(), calls))
+    stop[0] = True
+    th.join()
+    job.cache.close()
+    out = []
+    for name, t0, t1, calls in phases:
+        # samples wholly inside the phase, after its first second (the clock settles)
+        v = [x for a, b, x in samples if a >= t0 + 1.0 and b <= t1]
+        if not v:
+            continue
+        out.append({"phase": name, "samples": len(v), "calls": calls,
+                    "socket_power_W": statistics.median(x[0] for x in v),
+                    "gfx_clock_MHz": round(statistics.median(x[1] for x in v))})
+    return {"sampler": " ".join(cmd), "phase_seconds": secs, "phases": out}
+
+
 def ngram_ban_timing(torch, rswa, requests=64, vocab=129280, ngram=35, window=128, reps=200):
     """Time of one rswa_ngram_ban call at the page's sizes: 64 requests,
     129,280-token vocabulary, n = 35 inside a 128-token window, bf16 logits.
@@ -670,6 +758,8 @@ def main():
                     help="skip the prefill-kernel timing on the 100-page document")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0)
+    ap.add_argument("--power", action="store_true",
+                    help="only sample socket power and clock during prefill, MFMA-only and HBM loads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) for counter calibration")
     args = ap.parse_args()
@@ -697,6 +787,10 @@ def main():
 
     if args.serve:
         print(json.dumps(serve(torch, rswa, args)), flush=True)
+        return
+
+    if args.power:
+        print(json.dumps(power_clock(torch, rswa)), flush=True)
         return
 
     w = W.ALL[args.workload]
