@@ -323,6 +323,20 @@ def measured_peaks(torch, rswa, read_gib: int = 4):
     b.synchronize()
     read_gbs = nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
     del buf
+    # A plain device copy (torch): the ceiling for the prefill cache write,
+    # which reads k and v and writes them into the pool.
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a.record(stream)
+    reps = 20
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    b.synchronize()
+    copy_gbs = 2 * src.numel() * 2 * reps / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, dst
     n = 8192
     x = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
     y = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
@@ -355,6 +369,8 @@ def measured_peaks(torch, rswa, read_gib: int = 4):
         del ops
     torch.cuda.empty_cache()
     return {"hbm_read_GBps": round(read_gbs, 1), "hbm_read": f"rswa_measure_read over {read_gib} GiB",
+            "device_copy_GBps": round(copy_gbs, 1),
+            "device_copy": "torch copy_ of 1 GiB, read + write bytes",
             "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
             "bf16_gemm": f"torch.matmul {n}x{n}x{n} bf16",
             "bf16_mfma_random_TFLOPs": round(mfma["random"], 1),
