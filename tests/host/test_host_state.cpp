@@ -567,6 +567,116 @@ static void test_admission() {
   CHECK(st.check_retire(1, nullptr, &err) == RSWA_E_ARG);
 }
 
+// Seeded random batches (heads, window, batch size and prefill lengths,
+// including empty prefills): the decode plan tiles every request's keys
+// exactly once and keeps the split-size rules; the prefill plan launches
+// every (request, query tile, head) block exactly once, each (request, head)
+// group on one XCD with its longest tiles first when there are enough groups.
+static void test_plans_randomized() {
+  uint64_t s = 0x9e3779b97f4a7c15ull;
+  auto rnd = [&](int lo, int hi) {  // xorshift64, uniform enough in [lo, hi]
+    s ^= s << 13;
+    s ^= s >> 7;
+    s ^= s << 17;
+    return lo + (int)(s % (uint64_t)(hi - lo + 1));
+  };
+  const int windows[] = {1, 2, 8, 128, 300};
+  int one_round = 0, long_splits = 0, by_group = 0, by_block = 0;  // cases seen per rule
+  for (int it = 0; it < 300; ++it) {
+    rswa_config rc = base_cfg();
+    rc.num_layers = 1;
+    rc.num_heads = rnd(1, 16);
+    rc.window = windows[rnd(0, 4)];
+    const int n = rnd(1, 64);
+    rc.max_requests = n;
+    rc.max_positions = 32768;
+    std::vector<int32_t> ids(n), pl(n);
+    std::vector<int64_t> base(n);
+    int64_t rows = 0, tokens = 0;
+    for (int i = 0; i < n; ++i) {
+      ids[i] = i;
+      pl[i] = rnd(0, 1) ? rnd(0, 300) : rnd(1, 20000);
+      base[i] = rows;
+      rows += pl[i] + rc.window;
+      tokens += pl[i];
+    }
+    rc.num_slots = rows;
+    rc.max_prefill_tokens = std::max<int64_t>(1, tokens);
+    HostState st(resolved(rc));
+    register_all(st, n, ids.data(), pl.data(), base.data());
+    const int64_t heads = rc.num_heads;
+
+    const DecodePlan p = st.plan_decode(n, ids.data());
+    check_tiling(p, n, pl.data(), base.data(), rc.window, rswa_key0);
+    int64_t keys = 0, longest = 0;
+    for (int i = 0; i < n; ++i) {
+      keys += pl[i] + rc.window;
+      longest = std::max<int64_t>(longest, pl[i] + rc.window);
+    }
+    CHECK(p.num_splits() <= st.config().max_splits);
+    const int64_t sz = p.split_tokens;
+    if (sz < longest) {
+      // a forced split size: a multiple of 64 that fits the rule it follows
+      CHECK(sz % kSplitQuantum == 0);
+      if (keys * heads <= kOneRoundKeys) {
+        CHECK(p.num_splits() * heads <= kDecodeWaves || p.num_splits() == st.config().max_splits);
+        ++one_round;
+      } else {
+        CHECK(sz >= kLongSplitKeys);
+        ++long_splits;
+      }
+    }
+
+    for (int tile : {64, 256}) {
+      const PrefillPlan pp = st.plan_prefill(n, pl.data(), tile);
+      std::set<std::tuple<int, int, int>> seen;
+      std::map<std::pair<int, int>, std::vector<std::pair<int64_t, int>>> where;
+      for (int64_t i = 0; i < pp.num_tiles(); ++i) {
+        const int b = pp.tiles[2 * i];
+        if (b < 0) continue;
+        const uint32_t slot = (uint32_t)pp.tiles[2 * i + 1];
+        const int qt = (int)(slot >> 16), h = (int)(slot & 0xffffu);
+        CHECK(b < n && h < heads && qt * tile < pl[b]);
+        CHECK(seen.insert({b, qt, h}).second);
+        where[{b, h}].push_back({i, qt});
+      }
+      int64_t expect = 0;
+      for (int i = 0; i < n; ++i) expect += heads * ((pl[i] + tile - 1) / tile);
+      CHECK((int64_t)seen.size() == expect);
+      CHECK(pp.num_tiles() <= st.config().max_prefill_blocks());
+      CHECK(pp.num_tiles() == 0 || pp.tiles[2 * (pp.num_tiles() - 1)] >= 0);  // no trailing empty slot
+      CHECK(pp.num_tiles() <= 2 * expect + 64);  // padding stays bounded
+      bool grouped = true;
+      for (auto &kv : where)
+        for (size_t k = 0; k < kv.second.size(); ++k)
+          grouped = grouped && kv.second[k].first % kNumXcds == kv.second[0].first % kNumXcds;
+      if (grouped && (int64_t)where.size() >= kXcdAffinityGroups) ++by_group;
+      if (!grouped) ++by_block;
+      if (grouped) {
+        // each (request, head) on one XCD: its query tiles longest first
+        for (auto &kv : where)
+          for (size_t k = 0; k < kv.second.size(); ++k)
+            CHECK(kv.second[k].second == (int)(kv.second.size() - 1 - k));
+      } else {
+        // blocks assigned one by one, longest first: along each XCD's
+        // slots the work (query tiles up to the block's) never grows
+        for (int x = 0; x < kNumXcds; ++x) {
+          int prev = 1 << 30;
+          for (int64_t i = x; i < pp.num_tiles(); i += kNumXcds) {
+            if (pp.tiles[2 * i] < 0) continue;
+            const int w = (int)((uint32_t)pp.tiles[2 * i + 1] >> 16) + 1;
+            CHECK(w <= prev);
+            prev = w;
+          }
+        }
+      }
+    }
+  }
+  CHECK(one_round > 0 && long_splits > 0 && by_group > 0 && by_block > 0);
+  std::printf("randomized plans: %d one-round, %d long-split decode plans; %d grouped, %d per-block prefill plans\n",
+              one_round, long_splits, by_group, by_block);
+}
+
 int main() {
   test_config();
   test_layout();
@@ -576,6 +686,7 @@ int main() {
   test_fused_step();
   test_prefill_tile_index_limit();
   test_decode_plan();
+  test_plans_randomized();
   test_step_completion();
   test_chunked_prefill();
   test_admission();
