@@ -226,6 +226,44 @@ def test_merge_of_many_splits(dtype, head_dim, fused):
     _check_run(sc, res, inputs, check_pool=False)
 
 
+def _random_config(seed: int):
+    """One seeded draw over the parameters the path takes: dtype and head
+    dimension, heads, window, ragged prefill lengths (empty and tile-edge
+    ones included), staggered starts, paged or contiguous pool, fused or
+    separate ring write, R-SWA or the standard-window baseline, and the
+    split size (0: the planner's)."""
+    rng = np.random.default_rng([2024, seed])
+    dtype, head_dim = [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)][int(rng.integers(4))]
+    n = int(rng.integers(1, 7))
+    window = int(rng.choice([1, 3, 16, 64, 130]))
+    lens = tuple(int(rng.choice([0, 1, 63, 64, 65, 257])) if rng.random() < 0.5
+                 else int(rng.integers(1, 1500)) for _ in range(n))
+    w = dataclasses.replace(
+        SMALL_RAGGED, dtype=dtype, head_dim=head_dim, heads=int(rng.integers(1, 6)),
+        prefill_lens=lens, window=window,
+        start_steps=tuple(int(rng.integers(0, 2 * window + 3)) for _ in range(n)),
+        decode_steps=int(rng.integers(5, 30)), paged=bool(rng.integers(2)), wid=700 + seed,
+        v_std_ratio=1.0 if dtype == "f32" else SMALL_RAGGED.v_std_ratio)
+    return (w, bool(rng.integers(2)), str(rng.choice(["rswa", "swa"], p=[0.7, 0.3])),
+            int(rng.choice([0, 64, 128, 256])))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configs(seed):
+    """Seeded configurations across the parameter space, every prefill row,
+    every decode step of every request and layer, the ring state and the
+    pool against the oracle."""
+    w, fused, attention, split = _random_config(seed)
+    print(f"random config {seed}: {w.dtype} D={w.head_dim} H={w.heads} W={w.window} "
+          f"P={w.prefill_lens} starts={w.start_steps} steps={w.decode_steps} paged={w.paged} "
+          f"fused={fused} {attention} split={split}", flush=True)
+    sc = H.Scenario(w, steps=w.decode_steps, check_steps=range(w.decode_steps), split_tokens=split,
+                    fused=fused, attention=attention)
+    inputs = H.Inputs(w)
+    res = H.run_gpu(sc, inputs)
+    _check_run(sc, res, inputs)
+
+
 def test_position_limit_is_reported_and_state_kept():
     from kv_cache_management_amd.rswa import RSWAError, RSWA_E_POSITION
 
