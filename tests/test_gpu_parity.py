@@ -248,7 +248,7 @@ def _random_config(seed: int):
             int(rng.choice([0, 64, 128, 256])))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_configs(seed):
     """Seeded configurations across the parameter space, every prefill row,
     every decode step of every request and layer, the ring state and the
