@@ -393,6 +393,14 @@ DecodePlan HostState::plan_decode(int32_t n, const int32_t *ids) const {
       p.splits.push_back(d);
     }
   }
+  const int64_t tasks = (int64_t)p.num_splits() * heads;
+  if (tasks <= kDecodeCUs)
+    p.waves_per_block = 1;
+  else if (tasks <= kDecodeWaves)
+    p.waves_per_block = kDecodeWavesPerBlock;
+  else
+    p.waves_per_block = (int32_t)std::clamp<int64_t>(resident_waves_ / kDecodeCUs, kDecodeWavesPerBlock,
+                                                     kDecodeMaxWavesPerBlock);
   return p;
 }
 

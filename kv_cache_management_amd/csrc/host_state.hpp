@@ -31,9 +31,13 @@ constexpr int kSplitQuantum = 64;      // forced split sizes are multiples of th
 // block per CU), with the shortest split length that fits; larger batches use
 // kLongSplitKeys-key splits, lengthened until every wave of the launch is
 // resident at once: blocks that do not fit start only when others finish
-// and then stream alone, at the end of the step.
+// and then stream alone, at the end of the step.  Those launches use blocks
+// of as many waves as a CU holds, one block per CU: blocks of four landed
+// two or three to a CU, unevenly, and streamed ~3 % slower.  A launch of at
+// most one wave per CU uses single-wave blocks, one per CU.
 constexpr int kDecodeWaves = 1024;          // 256 CUs x 4 SIMDs
 constexpr int kDecodeWavesPerBlock = 4;
+constexpr int kDecodeMaxWavesPerBlock = 12; // 3 waves per SIMD x 4 SIMDs
 constexpr int kDecodeCUs = 256;
 constexpr int kLongSplitKeys = 1024;
 constexpr int64_t kOneRoundKeys = (int64_t)kDecodeWaves * 1280;
@@ -127,6 +131,7 @@ struct RequestState {
 
 struct DecodePlan {
   int32_t split_tokens = 0;        // keys of the longest split
+  int32_t waves_per_block = kDecodeWavesPerBlock;  // launch shape, 1 .. kDecodeMaxWavesPerBlock
   std::vector<int32_t> split_off;  // n + 1
   std::vector<SplitDesc> splits;   // num_splits, entry-major
   int32_t num_splits() const { return (int32_t)splits.size(); }

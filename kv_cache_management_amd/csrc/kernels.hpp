@@ -55,6 +55,7 @@ struct DecodeArgs {
   int32_t n, heads, window, layer, num_splits;
   int32_t attention;          // RSWA_ATTENTION_RSWA or RSWA_ATTENTION_SWA
   int32_t advance;            // nonzero: this launch ends the step (t += 1 per entry)
+  int32_t wpb;                // waves per block, 1 .. kDecodeMaxWavesPerBlock
 };
 
 struct PrefillArgs {

@@ -549,6 +549,7 @@ int decode_impl(rswa_cache *c, int32_t layer, const void *q, const void *k_new, 
   a.window = c->cfg.window;
   a.layer = layer;
   a.num_splits = plan.num_splits();
+  a.wpb = plan.waves_per_block;
   a.attention = c->cfg.attention;
   hipStream_t s = (hipStream_t)stream;
   const int pi = noalloc ? -1 : c->prof_begin(RSWA_KERNEL_DECODE_SPLIT, s);

@@ -112,7 +112,7 @@ constexpr int kCoherent = 16;
 // that entry has read t.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool PAGED, bool FUSED>
-__global__ __launch_bounds__(256, RSWA_DECODE_MIN_BLOCKS) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeMaxWavesPerBlock, RSWA_DECODE_MIN_BLOCKS) void decode_split_kernel(DecodeArgs a) {
   constexpr int EPL = Vec16<T>::N;      // elements per 16-byte load
   constexpr int LPR = D / EPL;          // lanes per key row
   constexpr int TPI = 64 / LPR;         // key rows per load instruction
@@ -121,13 +121,13 @@ __global__ __launch_bounds__(256, RSWA_DECODE_MIN_BLOCKS) void decode_split_kern
   constexpr int DUP = LPR / NI;         // lanes holding each score
   constexpr int SH = Log2<DUP>::value;
   static_assert(CH <= 64, "chunk keys must fit one table load");
-  __shared__ float lds_p[4][64];
-  __shared__ int32_t lds_row[4][64];
-  __shared__ uint4 lds_new[FUSED ? 4 : 1][2][LPR];
+  __shared__ float lds_p[kDecodeMaxWavesPerBlock][64];
+  __shared__ int32_t lds_row[kDecodeMaxWavesPerBlock][64];
+  __shared__ uint4 lds_new[FUSED ? kDecodeMaxWavesPerBlock : 1][2][LPR];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int task = blockIdx.x * 4 + wid;
+  const int task = blockIdx.x * (int)(blockDim.x >> 6) + wid;  // blocks of 1 .. 12 waves
   if (task >= a.num_splits * a.heads) return;
   const int ks = task / a.heads;
   const int h = task % a.heads;
@@ -488,16 +488,17 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream
     using T = decltype(tv);
     constexpr int D = decltype(dv)::value;
     const int64_t tasks = (int64_t)a.num_splits * a.heads;
-    const dim3 grid((unsigned)((tasks + 3) / 4));
+    if (a.wpb < 1 || a.wpb > kDecodeMaxWavesPerBlock) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((tasks + a.wpb - 1) / a.wpb));
     const bool fused = a.k_new != nullptr;
     if (a.pool.table && fused)
-      hipLaunchKernelGGL((decode_split_kernel<T, D, true, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_split_kernel<T, D, true, true>), grid, dim3(64 * a.wpb), 0, s, a);
     else if (a.pool.table)
-      hipLaunchKernelGGL((decode_split_kernel<T, D, true, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_split_kernel<T, D, true, false>), grid, dim3(64 * a.wpb), 0, s, a);
     else if (fused)
-      hipLaunchKernelGGL((decode_split_kernel<T, D, false, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_split_kernel<T, D, false, true>), grid, dim3(64 * a.wpb), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_split_kernel<T, D, false, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_split_kernel<T, D, false, false>), grid, dim3(64 * a.wpb), 0, s, a);
     return hipGetLastError();
   });
 }
@@ -517,11 +518,11 @@ hipError_t decode_resident_waves(int dtype, int head_dim, int64_t *waves) {
     int fewest = 1 << 30;
     for (const void *f : k) {
       int blocks = 0;
-      const hipError_t r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, f, 256, 0);
+      const hipError_t r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, f, 64, 0);
       if (r != hipSuccess) return r;
       fewest = std::min(fewest, blocks);
     }
-    *waves = (int64_t)fewest * 4 * cus;
+    *waves = (int64_t)fewest * cus;  // single-wave blocks: waves per CU
     return hipSuccess;
   });
 }

@@ -390,6 +390,9 @@ static void test_decode_plan() {
   CHECK(st.resident_waves() == kDefaultResidentWaves);
   CHECK(p.split_tokens > kLongSplitKeys && p.split_tokens % kSplitQuantum == 0);
   CHECK(p.num_splits() * 10 <= st.resident_waves());
+  // all resident: blocks of as many waves as a CU holds, one block per CU
+  CHECK(p.waves_per_block == kDecodeMaxWavesPerBlock);
+  CHECK((p.num_splits() * 10 + p.waves_per_block - 1) / p.waves_per_block <= kDecodeCUs);
   {
     // one 64-key step shorter would not fit
     int64_t k = 0;
@@ -423,6 +426,7 @@ static void test_decode_plan() {
     check_tiling(q, 8, p8.data(), b8.data(), 128, rswa_key0);
     CHECK(q.num_splits() * 10 <= kDecodeCUs * kDecodeWavesPerBlock);
     CHECK(q.split_tokens == 384 && q.split_off[1] == 12);
+    CHECK(q.waves_per_block == kDecodeWavesPerBlock);  // 960 waves: 240 blocks of four
   }
   // Forced split size: fixed-length splits, the last one shorter; a
   // too-small max_splits is reported.
@@ -572,6 +576,23 @@ static void test_admission() {
 // exactly once and keeps the split-size rules; the prefill plan launches
 // every (request, query tile, head) block exactly once, each (request, head)
 // group on one XCD with its longest tiles first when there are enough groups.
+// The launch shape the decode plan picks for its wave count.
+static void check_launch_shape(const DecodePlan &p, int64_t heads, int64_t resident) {
+  const int64_t tasks = (int64_t)p.num_splits() * heads;
+  const int wpb = p.waves_per_block;
+  CHECK(wpb >= 1 && wpb <= kDecodeMaxWavesPerBlock);
+  if (tasks <= kDecodeCUs)
+    CHECK(wpb == 1);
+  else if (tasks <= kDecodeWaves)
+    CHECK(wpb == kDecodeWavesPerBlock);
+  else
+    CHECK(wpb == std::min<int64_t>(kDecodeMaxWavesPerBlock,
+                                   std::max<int64_t>(kDecodeWavesPerBlock, resident / kDecodeCUs)));
+  // a launch whose waves are all resident puts at most one block on a CU
+  if (tasks <= resident && resident / kDecodeCUs <= kDecodeMaxWavesPerBlock)
+    CHECK((tasks + wpb - 1) / wpb <= kDecodeCUs);
+}
+
 static void test_plans_randomized() {
   uint64_t s = 0x9e3779b97f4a7c15ull;
   auto rnd = [&](int lo, int hi) {  // xorshift64, uniform enough in [lo, hi]
@@ -608,6 +629,7 @@ static void test_plans_randomized() {
 
     const DecodePlan p = st.plan_decode(n, ids.data());
     check_tiling(p, n, pl.data(), base.data(), rc.window, rswa_key0);
+    check_launch_shape(p, heads, st.resident_waves());
     int64_t keys = 0, longest = 0;
     for (int i = 0; i < n; ++i) {
       keys += pl[i] + rc.window;
