@@ -393,14 +393,11 @@ DecodePlan HostState::plan_decode(int32_t n, const int32_t *ids) const {
       p.splits.push_back(d);
     }
   }
+  // Launch shape: the fewest waves per block that give every CU at most one
+  // block, within what a CU holds.
   const int64_t tasks = (int64_t)p.num_splits() * heads;
-  if (tasks <= kDecodeCUs)
-    p.waves_per_block = 1;
-  else if (tasks <= kDecodeWaves)
-    p.waves_per_block = kDecodeWavesPerBlock;
-  else
-    p.waves_per_block = (int32_t)std::clamp<int64_t>(resident_waves_ / kDecodeCUs, kDecodeWavesPerBlock,
-                                                     kDecodeMaxWavesPerBlock);
+  const int64_t per_cu = std::clamp<int64_t>(resident_waves_ / kDecodeCUs, 1, kDecodeMaxWavesPerBlock);
+  p.waves_per_block = (int32_t)std::clamp<int64_t>(ceil_div(tasks, kDecodeCUs), 1, per_cu);
   return p;
 }
 

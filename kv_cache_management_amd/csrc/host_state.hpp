@@ -31,10 +31,11 @@ constexpr int kSplitQuantum = 64;      // forced split sizes are multiples of th
 // block per CU), with the shortest split length that fits; larger batches use
 // kLongSplitKeys-key splits, lengthened until every wave of the launch is
 // resident at once: blocks that do not fit start only when others finish
-// and then stream alone, at the end of the step.  Those launches use blocks
-// of as many waves as a CU holds, one block per CU: blocks of four landed
-// two or three to a CU, unevenly, and streamed ~3 % slower.  A launch of at
-// most one wave per CU uses single-wave blocks, one per CU.
+// and then stream alone, at the end of the step.  A launch is shaped as one
+// block per CU with the fewest waves per block that allows (single waves
+// for at most one wave per CU, four for a full one-round batch, twelve for
+// one of every resident wave): blocks of four landed two or three to a CU,
+// unevenly, and streamed ~3 % slower.
 constexpr int kDecodeWaves = 1024;          // 256 CUs x 4 SIMDs
 constexpr int kDecodeWavesPerBlock = 4;
 constexpr int kDecodeMaxWavesPerBlock = 12; // 3 waves per SIMD x 4 SIMDs

@@ -579,18 +579,17 @@ static void test_admission() {
 // The launch shape the decode plan picks for its wave count.
 static void check_launch_shape(const DecodePlan &p, int64_t heads, int64_t resident) {
   const int64_t tasks = (int64_t)p.num_splits() * heads;
-  const int wpb = p.waves_per_block;
-  CHECK(wpb >= 1 && wpb <= kDecodeMaxWavesPerBlock);
-  if (tasks <= kDecodeCUs)
-    CHECK(wpb == 1);
-  else if (tasks <= kDecodeWaves)
+  const int64_t wpb = p.waves_per_block;
+  const int64_t per_cu = std::min<int64_t>(kDecodeMaxWavesPerBlock, std::max<int64_t>(1, resident / kDecodeCUs));
+  CHECK(wpb >= 1 && wpb <= per_cu);
+  const int64_t blocks = (tasks + wpb - 1) / wpb;
+  // at most one block per CU whenever a CU can hold the waves that needs,
+  // with the fewest waves per block that achieve it
+  if (tasks <= per_cu * kDecodeCUs) CHECK(blocks <= kDecodeCUs);
+  if (wpb > 1) CHECK((tasks + wpb - 2) / (wpb - 1) > kDecodeCUs);
+  if (tasks <= kDecodeCUs) CHECK(wpb == 1);
+  if (tasks > kDecodeCUs * (kDecodeWavesPerBlock - 1) && tasks <= kDecodeWaves)
     CHECK(wpb == kDecodeWavesPerBlock);
-  else
-    CHECK(wpb == std::min<int64_t>(kDecodeMaxWavesPerBlock,
-                                   std::max<int64_t>(kDecodeWavesPerBlock, resident / kDecodeCUs)));
-  // a launch whose waves are all resident puts at most one block on a CU
-  if (tasks <= resident && resident / kDecodeCUs <= kDecodeMaxWavesPerBlock)
-    CHECK((tasks + wpb - 1) / wpb <= kDecodeCUs);
 }
 
 static void test_plans_randomized() {
