@@ -14,20 +14,32 @@ from oracle import rswa_oracle as O
 pytestmark = pytest.mark.gpu
 
 
-def _make(torch, R, plens, window, layers, heads, dim, table=None):
+def _make(torch, R, plens, window, layers, heads, dim, table=None, max_positions=4096):
     n = len(plens)
     rows = sum(p + window for p in plens)
     c = R.RSWACache(layers, heads, dim, window, max_requests=n, num_slots=rows, dtype="bf16",
-                    max_positions=4096, slot_table=table, max_prefill_tokens=sum(plens))
+                    max_positions=max_positions, slot_table=table, max_prefill_tokens=sum(plens))
     return c
 
 
+# (prompt lengths, window, layers, heads): a few small requests (single-wave
+# blocks), a one-round batch (blocks of four) and a batch beyond one round
+# (blocks of eight, one per CU).
+GRAPH_CONFIGS = {
+    "small": ([40, 0, 300], 16, 2, 3),
+    "one_round": ([5000 - 37 * i for i in range(24)], 128, 1, 10),
+    "beyond_one_round": ([6000 - 29 * i for i in range(32)], 128, 1, 10),
+}
+
+
+@pytest.mark.parametrize("config", sorted(GRAPH_CONFIGS))
 @pytest.mark.parametrize("paged", [False, True])
-def test_graph_replay_matches_eager(paged):
+def test_graph_replay_matches_eager(paged, config):
     import torch
     from kv_cache_management_amd import rswa as R
 
-    plens, window, layers, heads, dim = [40, 0, 300], 16, 2, 3, 128
+    plens, window, layers, heads = GRAPH_CONFIGS[config]
+    dim = 128
     n = len(plens)
     K, replays = 4, 6
     rows = sum(p + window for p in plens)
@@ -40,7 +52,8 @@ def test_graph_replay_matches_eager(paged):
     tot = sum(plens)
     pf = [[torch.randn((tot, heads, dim), device=dev, generator=gen).bfloat16() for _ in range(3)]
           for _ in range(layers)]
-    caches = [_make(torch, R, plens, window, layers, heads, dim, table) for _ in range(2)]
+    caches = [_make(torch, R, plens, window, layers, heads, dim, table, max_positions=8192)
+              for _ in range(2)]
     bases = np.concatenate([[0], np.cumsum([p + window for p in plens])[:-1]]).astype(np.int64)
     scratch = torch.empty((tot, heads, dim), device=dev, dtype=torch.bfloat16)
     for c in caches:
