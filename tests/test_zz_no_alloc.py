@@ -109,3 +109,45 @@ def test_noalloc_refuses_partials_beyond_the_scratch():
     torch.cuda.synchronize()
     assert list(c.get_state([0])[2]) == [p + 1]
     c.close()
+
+
+def test_noalloc_matches_fused_on_a_large_batch():
+    """Same comparison on a batch beyond one round (32 requests of ~6000
+    keys, 10 heads: 1920 (split, head) partials, blocks of eight waves), then
+    a one-round batch of 16 of them (blocks of four): outputs identical."""
+    import torch
+    from kv_cache_management_amd import rswa as R
+
+    torch.cuda.set_device(0)
+    plens = [6000 - 29 * i for i in range(32)]
+    heads, window = 10, 128
+    rows = sum(p + window for p in plens)
+    bases = np.concatenate([[0], np.cumsum([p + window for p in plens])[:-1]]).astype(np.int64)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    x = [torch.randn((sum(plens), heads, D), device="cuda", generator=gen).mul_(D ** -0.5).bfloat16()
+         for _ in range(3)]
+    out = torch.empty_like(x[0])
+    caches = []
+    for _ in range(2):
+        c = R.RSWACache(1, heads, D, window, max_requests=len(plens), num_slots=rows, dtype="bf16",
+                        max_positions=8192, max_prefill_tokens=sum(plens), pool_fill=float("nan"))
+        c.prefill(0, list(range(len(plens))), plens, bases.tolist(), *x, out)
+        caches.append(c)
+    ref, dut = caches
+    for step, batch in enumerate((list(range(32)), list(range(0, 32, 2)))):
+        for c in (ref, dut):
+            c.set_batch(batch)
+        q, k, v = (torch.randn((len(batch), heads, D), device="cuda", generator=gen).mul_(D ** -0.5).bfloat16()
+                   for _ in range(3))
+        o_ref = torch.full((len(batch), heads, D), float("nan"), device="cuda", dtype=torch.bfloat16)
+        o_dut = torch.full_like(o_ref, float("nan"))
+        ref.decode_step_fused(0, q, k, v, o_ref)
+        dut.decode_step_fused_noalloc(0, q, k, v, o_dut)
+        ref.advance()
+        dut.advance()
+        torch.cuda.synchronize()
+        assert torch.isfinite(o_ref.float()).all()
+        assert torch.equal(o_ref, o_dut), f"call {step + 1}: noalloc output differs"
+    ref.close()
+    dut.close()
