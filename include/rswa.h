@@ -324,12 +324,16 @@ int rswa_ngram_ban(const int32_t *tokens, int64_t token_stride, const int32_t *l
 
 /* Measurement helper, not part of the attention path: reads `bytes` of
  * device memory at `buf` with the decode kernel's 16-byte non-temporal
- * loads, 4096 blocks of 256 threads, each block one contiguous chunk, and
- * writes one word per block to `sink` (device, at least 4096 uint32), so
- * that the bytes / kernel time it reaches is the read rate the decode
- * kernel's HBM figure can be set against.  Asynchronous on `stream`.
+ * loads, one block of 256 threads (one wavefront per SIMD) per CU, the
+ * wavefronts sweeping the buffer together in 8 KB slabs, so that the
+ * bytes / kernel time it reaches is the read rate the decode kernel's HBM
+ * figure can be set against.  Writes to `sink` (device, at least
+ * RSWA_MEASURE_SINK_WORDS uint32) one word per wavefront: the wrapping
+ * 32-bit sum of the 32-bit words it read, so for a size that is a multiple
+ * of 16 bytes the words written sum to the buffer's word sum; words past
+ * the grid's wavefronts are left untouched.  Asynchronous on `stream`.
  * Errors: RSWA_E_ARG (null pointer or zero bytes), RSWA_E_UNSUPPORTED
- * (bytes of 16 TiB or more), RSWA_E_HIP (launch failure). */
+ * (bytes of 16 TiB or more), RSWA_E_HIP (device query or launch failure). */
 enum { RSWA_MEASURE_SINK_WORDS = 4096 };
 int rswa_measure_read(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
 

@@ -1,8 +1,10 @@
 // Measurement helpers, not part of the attention path:
 //   - a plain streaming read of device memory, giving the HBM read rate that
 //     this GPU reaches with the same load instruction the decode kernel uses
-//     (16-byte non-temporal buffer loads, large contiguous chunk per
-//     wavefront);
+//     (16-byte non-temporal buffer loads): one wavefront per SIMD, all of
+//     them sweeping the buffer together in 8 KB slabs, the pattern that
+//     reads fastest here (one contiguous chunk per wavefront, 2048 chunks in
+//     flight, read ~6 % slower);
 //   - a matrix-core loop with the prefill kernel's instruction
 //     (v_mfma_f32_32x32x16_bf16) on operands taken from a caller buffer, two
 //     wavefronts per SIMD, nothing else: the bf16 MFMA rate this GPU
@@ -11,6 +13,7 @@
 //     zeros or repeated values).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "device_common.hpp"
@@ -21,38 +24,33 @@ namespace {
 
 using namespace dev;
 
-constexpr int kReadBlocks = 4096;
-constexpr int kReadThreads = 256;
-constexpr int kUnroll = 8;
+constexpr int kReadThreads = 256;  // four wavefronts: one per SIMD of the CU
+constexpr int kUnroll = 8;         // 16-byte loads in flight per lane
+constexpr uint32_t kSlab = 64u * 16u * kUnroll;  // bytes of one wavefront pass
 
-// Block b reads the b-th of kReadBlocks equal contiguous chunks (the tail
-// past `bytes` reads zero through the buffer resource bound).  Each wave
-// streams its own quarter of the chunk with kUnroll 16-byte loads in flight
-// per lane.
+// Wavefront w reads slabs w, w + W, w + 2W, ... (W wavefronts in the grid),
+// so at any moment the grid reads one contiguous stretch of the buffer.
+// Loads past the end are cut off by the slab's resource bound.  Each
+// wavefront writes the wrapping 32-bit sum of the words it read, so for a
+// size that is a multiple of 16 bytes the sink words sum to the buffer's
+// word sum: every byte is read exactly once.
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const char *buf, uint64_t bytes,
-                                                                   uint64_t chunk, uint32_t *sink) {
-  const uint64_t b0 = (uint64_t)blockIdx.x * chunk;
-  if (b0 >= bytes) {
-    if (threadIdx.x == 0) sink[blockIdx.x] = 0;
-    return;
-  }
-  const uint64_t len = bytes - b0 < chunk ? bytes - b0 : chunk;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(buf + b0, (uint32_t)len);
-  const int w = threadIdx.x >> 6;
+                                                                   uint32_t *sink) {
   const int lane = threadIdx.x & 63;
-  const uint32_t wchunk = (uint32_t)(chunk / 4);
+  const uint64_t wave = (uint64_t)blockIdx.x * (kReadThreads / 64) + (threadIdx.x >> 6);
+  const uint64_t stride = (uint64_t)gridDim.x * (kReadThreads / 64) * kSlab;
   uint32_t acc = 0;
-  for (uint32_t off = (uint32_t)w * wchunk; off < (uint32_t)(w + 1) * wchunk;
-       off += 64u * 16u * kUnroll) {
+  for (uint64_t s0 = wave * kSlab; s0 < bytes; s0 += stride) {
+    const uint64_t left = bytes - s0;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(buf + s0, left < kSlab ? (uint32_t)left : kSlab);
     uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = buf_load16<2>(r, off + (uint32_t)(u * 64 + lane) * 16u);
+    for (int u = 0; u < kUnroll; ++u) v[u] = buf_load16<2>(r, (uint32_t)(u * 64 + lane) * 16u);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < kUnroll; ++u) acc += v[u].x + v[u].y + v[u].z + v[u].w;
   }
-  // Keep the loads live: one word per block.
-  acc = (uint32_t)__shfl_xor((int)acc, 1) ^ acc;
-  if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+  for (int o = 32; o > 0; o >>= 1) acc += (uint32_t)__shfl_xor((int)acc, o);
+  if (lane == 0) sink[wave] = acc;
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -89,14 +87,15 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_loop_kernel(const bf16x8 *o
 
 extern "C" int rswa_measure_read(const void *buf, uint64_t bytes, uint32_t *sink, void *stream) {
   if (!buf || !sink || bytes == 0) return RSWA_E_ARG;
-  // Equal chunks, a multiple of one wave pass (64 lanes x 16 B x kUnroll)
-  // per wave, each below 4 GiB for the 32-bit buffer offsets.
-  const uint64_t quantum = 4ull * 64 * 16 * rswa::kUnroll;
-  uint64_t chunk = (bytes + rswa::kReadBlocks - 1) / rswa::kReadBlocks;
-  chunk = (chunk + quantum - 1) / quantum * quantum;
-  if (chunk >= (1ull << 32)) return RSWA_E_UNSUPPORTED;
-  hipLaunchKernelGGL(rswa::stream_read_kernel, dim3(rswa::kReadBlocks), dim3(rswa::kReadThreads), 0,
-                     (hipStream_t)stream, (const char *)buf, bytes, chunk, sink);
+  if (bytes >= (1ull << 44)) return RSWA_E_UNSUPPORTED;
+  // One block (one wavefront per SIMD) per CU, one sink word per wavefront.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return RSWA_E_HIP;
+  const int blocks = std::min(cus, RSWA_MEASURE_SINK_WORDS / (rswa::kReadThreads / 64));
+  hipLaunchKernelGGL(rswa::stream_read_kernel, dim3(blocks), dim3(rswa::kReadThreads), 0,
+                     (hipStream_t)stream, (const char *)buf, bytes, sink);
   return hipGetLastError() == hipSuccess ? RSWA_OK : RSWA_E_HIP;
 }
 

@@ -32,13 +32,22 @@ def test_measure_mfma_exact_on_constant_operands(value, iters):
     assert torch.all(sink == want), (sink[:4].tolist(), want)
 
 
-def test_measure_read_runs_on_a_ragged_buffer():
+@pytest.mark.parametrize("nbytes", [(3 << 20) + 48, 16, (64 << 20) + 8192 * 3 + 16])
+def test_measure_read_reads_every_byte_once(nbytes):
+    """The sink words (one wrapping 32-bit sum per wavefront, untouched words
+    left at zero) sum to the buffer's 32-bit word sum: every byte of a
+    buffer whose size is no multiple of the 8 KB slab is read exactly once."""
+    import numpy as np
     import torch
 
     R = _rswa()
-    nbytes = (3 << 20) + 48
-    buf = torch.full((nbytes,), 7, device="cuda", dtype=torch.uint8)
-    sink = torch.empty(R.RSWA_MEASURE_SINK_WORDS, device="cuda", dtype=torch.int32)
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    buf = torch.from_numpy(host).to("cuda")
+    sink = torch.zeros(R.RSWA_MEASURE_SINK_WORDS, device="cuda", dtype=torch.int32)
     st = R.rswa_measure_read(buf.data_ptr(), nbytes, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
     assert st == 0, R.load().rswa_status_string(st)
     torch.cuda.synchronize()
+    got = int(sink.cpu().numpy().view(np.uint32).astype(np.uint64).sum()) % (1 << 32)
+    want = int(host.view(np.uint32).astype(np.uint64).sum()) % (1 << 32)
+    assert got == want
